@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""Attention backward benchmark on one MI355X.
+
+One step = one full backward pass (preprocess -> main -> postprocess) over one
+batch of seeded synthetic inputs already resident in HBM; O and LSE come from
+one untimed forward.  Prints ONE JSON line on stdout:
+
+  metric/value/unit    backward TFLOP/s, counted as 10*b*h*Sq*Sk*d (halved
+                       when causal), over the wall clock of K steps bracketed
+                       by torch.cuda.synchronize();
+  roofline             the main kernel (the dominant one) against the MI355X
+                       dense fp16/bf16 matrix-core peak, its duration taken
+                       with HIP events on the launch stream inside the timed
+                       region; HBM traffic from the committed rocprofv3
+                       FETCH_SIZE/WRITE_SIZE measurement when it still matches
+                       the kernel source (else null);
+  cpu_baseline         the fp64 CPU oracle's backward on a bounded sample of
+                       the same workload (a few heads), scaled to TFLOP/s.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+MFMA_PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["flashattention_backward_pass_attn_amd/csrc/attn_bwd.h",
+                  "flashattention_backward_pass_attn_amd/csrc/attn_device.h"]
+TRAFFIC_FILE = "profiles/bwd_main_traffic_{workload}.json"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def workload_flops(w: workloads.Workload, inp) -> float:
+    if w.varlen:
+        return workloads.attention_flops(w.batch, w.heads_q, 0, 0, w.head_dim, w.causal,
+                                         lengths=[int(x) for x in inp["lengths_q"]])
+    return workloads.attention_flops(w.batch, w.heads_q, w.seqlen, w.seqlen, w.head_dim, w.causal)
+
+
+def load_traffic(workload: str):
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_source_sha():
+        log(f"traffic record {path} predates the current kernel source: reporting null")
+        return None
+    return rec
+
+
+def cpu_baseline(w: workloads.Workload, inp, budget_s: float):
+    """Time the oracle backward (given the oracle's own LSE) on whole heads until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    scale = 1.0 / math.sqrt(w.head_dim)
+    G = w.heads_q // w.heads_kv
+    done_flops, spent, heads = 0.0, 0.0, 0
+    # sample: query heads of sequence 0 in order (varlen: the sequences in order)
+    order = []
+    nseq = len(inp["lengths_q"]) if w.varlen else w.batch
+    for z in range(nseq):
+        for h in range(w.heads_q):
+            order.append((z, h))
+    for z, h in order:
+        if w.varlen:
+            a, e = int(inp["cu_seqlens_q"][z]), int(inp["cu_seqlens_q"][z + 1])
+            q, k, v, do = (inp[n][a:e] for n in ("q", "k", "v", "do"))
+            L = e - a
+            fl = workloads.attention_flops(1, 1, 0, 0, w.head_dim, w.causal, lengths=[L])
+            qh, kh, vh, doh = q[:, h], k[:, h // G], v[:, h // G], do[:, h]
+        else:
+            qh, kh, vh, doh = (inp[n][z, :, hh] for n, hh in (("q", h), ("k", h // G), ("v", h // G), ("do", h)))
+            fl = workloads.attention_flops(1, 1, w.seqlen, w.seqlen, w.head_dim, w.causal)
+        qh, kh, vh, doh = (np.asarray(x, dtype=np.float64) for x in (qh, kh, vh, doh))
+        _, lse = oracle.head_forward(qh, kh, vh, scale, w.causal)  # untimed: supplies LSE
+        t0 = time.perf_counter()
+        oracle.head_backward(qh, kh, vh, doh, scale, w.causal, lse=lse)
+        spent += time.perf_counter() - t0
+        done_flops += fl
+        heads += 1
+        if spent >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": done_flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} (sequence, query head) pairs of {w.name}, fp64 NumPy backward given the oracle's "
+                  f"LSE, {spent:.1f} s; flops counted as for the GPU",
+        "seconds": round(spent, 3),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=workloads.DEFAULT_BENCH_WORKLOAD, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--deterministic", action="store_true")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
+                    help="CPU time budget of the oracle sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (HBM counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the backward is independent "
+              "per (batch, head), so more GPUs would each run this same kernel on their share; no "
+              "multi-GPU figure is produced.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import flashattention_backward_pass_attn_amd as fa
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = workloads.make_workload_inputs(w.name)
+    tdt = {"fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+
+    def up(n):
+        return torch.from_numpy(np.ascontiguousarray(inp[n + "_bits"]).view(np.int16)).view(tdt).to(dev)
+
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    kw = {}
+    if w.varlen:
+        kw = dict(cu_seqlens_q=torch.from_numpy(inp["cu_seqlens_q"]).to(dev),
+                  cu_seqlens_k=torch.from_numpy(inp["cu_seqlens_k"]).to(dev),
+                  max_seqlen_q=int(inp["lengths_q"].max()), max_seqlen_k=int(inp["lengths_k"].max()))
+    scale = 1.0 / math.sqrt(w.head_dim)
+    o, lse = fa.attn_fwd(q, k, v, causal=w.causal, softmax_scale=scale, **kw)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    p = fa.make_params(q, k, w.causal, scale, args.deterministic, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"),
+                       kw.get("max_seqlen_q"), kw.get("max_seqlen_k"))
+    ws = torch.empty(max(fa.bwd_workspace_size(p), 256), dtype=torch.uint8, device=dev)
+    common = dict(causal=w.causal, softmax_scale=scale, deterministic=args.deterministic, dq=dq, dk=dk, dv=dv,
+                  workspace=ws, **kw)
+    flops = workload_flops(w, inp)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        fa.attn_bwd(q, k, v, o, lse, do, **common)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        e = ev[i]
+        e[0].record()
+        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_PREPROCESS, **common)
+        e[1].record()
+        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_MAIN, **common)
+        e[2].record()
+        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_POSTPROCESS, **common)
+        e[3].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
+    main_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    post_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    log(f"{w.name}: step {ms_per_step:.4f} ms (events: pre {pre_ms:.4f} main {main_ms:.4f} post {post_ms:.4f} ms)")
+
+    if args.copy_calibration:
+        n = 1 << 28  # 256 Mi floats = 1 GiB read + 1 GiB written
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n * 4} bytes read and written per copy kernel, 2 launches")
+
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (main_ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    traffic = load_traffic(w.name)
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
+        "kernel": "attn_bwd_main_kernel",
+        "kernel_ms": round(main_ms, 4),
+        "preprocess_ms": round(pre_ms, 4),
+        "postprocess_ms": round(post_ms, 4),
+    }
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        log("cpu baseline: timing the oracle backward on a bounded sample ...")
+        cpu = cpu_baseline(w, inp, args.cpu_baseline_seconds)
+    cfg = {"workload": w.name, "dtype": w.dtype, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+           "seqlen": (int(inp["lengths_q"].max()) if w.varlen else w.seqlen), "head_dim": w.head_dim,
+           "causal": w.causal, "varlen": w.varlen, "deterministic": args.deterministic,
+           "flop_per_step": flops, "parallelism": "single GPU"}
+    if w.varlen:
+        cfg["lengths"] = [int(x) for x in inp["lengths_q"]]
+    rec = {
+        "metric": "attention backward TFLOP/s (fp16/bf16, causal+non-causal) and % MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, see workloads/)",
+        "config": cfg,
+        "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,61 @@
+"""Compile the gfx950 HIP library libattn.so in-tree.
+
+``python -m flashattention_backward_pass_attn_amd.build`` (or ``build()``)
+runs hipcc on csrc/attn_api.hip, which includes every kernel, and writes
+``flashattention_backward_pass_attn_amd/libattn.so``.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
+SOURCES = [os.path.join(CSRC, "attn_api.hip")]
+HEADERS = [os.path.join(CSRC, f) for f in ("attn_device.h", "attn_fwd.h", "attn_bwd.h")] + [
+    os.path.join(ROOT, "include", "attn.h")
+]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-munsafe-fp-atomics",
+    # no packed-fp32 VALU instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+]
+
+
+def hipcc_path() -> str:
+    p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(p):
+        raise RuntimeError("hipcc not found: the HIP toolchain is required to build libattn.so")
+    return p
+
+
+def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH) -> str:
+    """Compile libattn.so (always recompiles).  Returns the library path."""
+    tmp = out_path + ".tmp"
+    cmd = [hipcc_path(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
+           *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libattn.so")
+    if verbose and res.stderr.strip():
+        sys.stderr.write(res.stderr)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

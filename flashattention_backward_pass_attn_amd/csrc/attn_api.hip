@@ -1,0 +1,288 @@
+// Host side of libattn.so: argument validation, workspace sizing and kernel
+// dispatch for the C ABI declared in include/attn.h.
+//
+// Validation mirrors the flash-attention CK mha_bwd.cpp page's mha_bwd checks
+// (fp16/bf16 only and all tensors of one dtype; contiguous last dimension;
+// batch > 0; head_dim % 8 == 0 and <= 256; heads_q % heads_kv == 0), returning
+// a status code instead of throwing.  Nothing is launched unless every check
+// passes.  Launch order follows the Hopper flash_bwd_launch_template.h page's
+// run_flash_bwd: preprocess, main, dQ postprocess, all on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "attn_bwd.h"
+#include "attn_device.h"
+#include "attn_fwd.h"
+
+namespace {
+
+using attn::Args;
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool strides_ok(const attn_strides& s, bool varlen) {
+  // 16-byte vector access needs every stride to be a multiple of 8 elements.
+  if (s.row <= 0 || s.head <= 0) return false;
+  if (s.row % 8 || s.head % 8) return false;
+  if (!varlen && (s.batch < 0 || s.batch % 8)) return false;
+  return true;
+}
+
+attn_status validate_common(const attn_params* p) {
+  if (!p) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->dtype != ATTN_FP16 && p->dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->batch <= 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->heads_q <= 0 || p->heads_kv <= 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->heads_q % p->heads_kv) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->head_dim <= 0 || p->head_dim % 8 || p->head_dim > 256) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->head_dim > 128) return ATTN_ERR_UNSUPPORTED;
+  if (p->seqlen_q < 0 || p->seqlen_k < 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->deterministic != 0 && p->deterministic != 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->softmax_scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  const bool vq = p->cu_seqlens_q != nullptr, vk = p->cu_seqlens_k != nullptr;
+  if (vq != vk) return ATTN_ERR_INVALID_ARGUMENT;
+  if (vq && (p->total_q < 0 || p->total_k < 0)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->heads_q > 65535 || p->batch > 65535) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+bool is_varlen(const attn_params* p) { return p->cu_seqlens_q != nullptr; }
+
+// Query-side / key-side tensors may be NULL only when they hold no element.
+bool q_empty(const attn_params* p) { return is_varlen(p) ? p->total_q == 0 : p->seqlen_q == 0; }
+bool k_empty(const attn_params* p) { return is_varlen(p) ? p->total_k == 0 : p->seqlen_k == 0; }
+
+int64_t stat_count(const attn_params* p) {
+  return is_varlen(p) ? (int64_t)p->heads_q * p->total_q
+                      : (int64_t)p->batch * p->heads_q * p->seqlen_q;
+}
+
+int num_kv_splits(const attn_params* p) { return (p->seqlen_k + attn::kBwdBN - 1) / attn::kBwdBN; }
+
+size_t acc_elems(const attn_params* p) { return (size_t)stat_count(p) * (size_t)p->head_dim; }
+
+size_t workspace_bytes(const attn_params* p) {
+  const size_t delta = round_up((size_t)stat_count(p) * sizeof(float), kAlign);
+  const size_t splits = p->deterministic ? (size_t)std::max(num_kv_splits(p), 1) : 1;
+  const size_t acc = round_up(splits * acc_elems(p) * sizeof(float), kAlign);
+  return delta + acc;
+}
+
+Args make_args(const attn_params* p) {
+  Args a;
+  std::memset(&a, 0, sizeof(a));
+  const bool vl = is_varlen(p);
+  a.cu_q = p->cu_seqlens_q;
+  a.cu_k = p->cu_seqlens_k;
+  auto set = [&](const attn_strides& s, int64_t& b, int64_t& r, int64_t& h) {
+    b = vl ? 0 : s.batch;
+    r = s.row;
+    h = s.head;
+  };
+  set(p->q, a.q_b, a.q_r, a.q_h);
+  set(p->k, a.k_b, a.k_r, a.k_h);
+  set(p->v, a.v_b, a.v_r, a.v_h);
+  set(p->o, a.o_b, a.o_r, a.o_h);
+  set(p->dout, a.do_b, a.do_r, a.do_h);
+  set(p->dq, a.dq_b, a.dq_r, a.dq_h);
+  set(p->dk, a.dk_b, a.dk_r, a.dk_h);
+  set(p->dv, a.dv_b, a.dv_r, a.dv_h);
+  a.batch = p->batch;
+  a.seqlen_q = p->seqlen_q;
+  a.seqlen_k = p->seqlen_k;
+  a.heads_q = p->heads_q;
+  a.heads_kv = p->heads_kv;
+  a.group = p->heads_q / p->heads_kv;
+  a.head_dim = p->head_dim;
+  a.total_q = vl ? p->total_q : 0;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * attn::kLog2e;
+  a.varlen = vl ? 1 : 0;
+  a.acc_split = (int64_t)acc_elems(p);
+  return a;
+}
+
+attn_status last_hip_status() {
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+// ---- dispatch helpers ------------------------------------------------------
+template <bool BF16, int D>
+void launch_fwd_d(const Args& a, bool causal, dim3 grid, hipStream_t st) {
+  if (causal)
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, false>), grid, dim3(256), 0, st, a);
+}
+
+template <bool BF16>
+void launch_fwd(const Args& a, int dtile, bool causal, dim3 grid, hipStream_t st) {
+  if (dtile == 64)
+    launch_fwd_d<BF16, 64>(a, causal, grid, st);
+  else
+    launch_fwd_d<BF16, 128>(a, causal, grid, st);
+}
+
+template <bool BF16, int D, bool CAUSAL>
+void launch_main_c(const Args& a, bool det, dim3 grid, hipStream_t st) {
+  if (det)
+    hipLaunchKernelGGL((attn::attn_bwd_main_kernel<BF16, D, CAUSAL, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn::attn_bwd_main_kernel<BF16, D, CAUSAL, false>), grid, dim3(256), 0, st, a);
+}
+
+template <bool BF16>
+void launch_main(const Args& a, int dtile, bool causal, bool det, dim3 grid, hipStream_t st) {
+  if (dtile == 64) {
+    if (causal) launch_main_c<BF16, 64, true>(a, det, grid, st);
+    else launch_main_c<BF16, 64, false>(a, det, grid, st);
+  } else {
+    if (causal) launch_main_c<BF16, 128, true>(a, det, grid, st);
+    else launch_main_c<BF16, 128, false>(a, det, grid, st);
+  }
+}
+
+template <bool BF16>
+void launch_post(const Args& a, bool causal, bool det, dim3 grid, hipStream_t st) {
+  if (det) {
+    if (causal) hipLaunchKernelGGL((attn::attn_bwd_post_kernel<BF16, true, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn::attn_bwd_post_kernel<BF16, false, true>), grid, dim3(256), 0, st, a);
+  } else {
+    if (causal) hipLaunchKernelGGL((attn::attn_bwd_post_kernel<BF16, true, false>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((attn::attn_bwd_post_kernel<BF16, false, false>), grid, dim3(256), 0, st, a);
+  }
+}
+
+int dtile_for(int head_dim) { return head_dim <= 64 ? 64 : 128; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* attn_version(void) { return "libattn gfx950 mfma32x32x16 bwd-kvstationary v1"; }
+
+attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const void* v, void* o,
+                     float* lse, void* stream) {
+  attn_status st = validate_common(p);
+  if (st != ATTN_OK) return st;
+  const bool qe = q_empty(p), ke = k_empty(p);
+  if ((!qe && (!q || !o || !lse)) || (!ke && (!k || !v))) return ATTN_ERR_INVALID_ARGUMENT;
+  const bool vl = is_varlen(p);
+  if (!strides_ok(p->q, vl) || !strides_ok(p->k, vl) || !strides_ok(p->v, vl) || !strides_ok(p->o, vl))
+    return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
+  if (p->seqlen_q == 0 || qe) return ATTN_OK;
+  Args a = make_args(p);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out_o = static_cast<uint16_t*>(o);
+  a.lse_out = lse;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  dim3 grid((p->seqlen_q + attn::kFwdBM - 1) / attn::kFwdBM, p->heads_q, p->batch);
+  const int dt = dtile_for(p->head_dim);
+  if (p->dtype == ATTN_BF16) launch_fwd<true>(a, dt, p->causal, grid, hs);
+  else launch_fwd<false>(a, dt, p->causal, grid, hs);
+  return last_hip_status();
+}
+
+attn_status attn_bwd_workspace_size(const attn_params* p, size_t* bytes) {
+  attn_status st = validate_common(p);
+  if (st != ATTN_OK) return st;
+  if (!bytes) return ATTN_ERR_INVALID_ARGUMENT;
+  *bytes = workspace_bytes(p);
+  return ATTN_OK;
+}
+
+attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                            void* workspace, size_t workspace_bytes_given, float* delta_out, void* stream,
+                            unsigned phases) {
+  if (phases == 0 || (phases & ~ATTN_PHASE_ALL) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  attn_status st = validate_common(p);
+  if (st != ATTN_OK) return st;
+  const bool qe = q_empty(p), ke = k_empty(p);
+  if ((!qe && (!q || !o || !lse || !dout || !dq)) || (!ke && (!k || !v || !dk || !dv)) || !workspace)
+    return ATTN_ERR_INVALID_ARGUMENT;
+  const bool vl = is_varlen(p);
+  const attn_strides* all[] = {&p->q, &p->k, &p->v, &p->o, &p->dout, &p->dq, &p->dk, &p->dv};
+  for (const attn_strides* s : all)
+    if (!strides_ok(*s, vl)) return ATTN_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return ATTN_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return ATTN_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes_given < workspace_bytes(p)) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+
+  Args a = make_args(p);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.lse_in = lse;
+  a.delta_out = delta_out;
+  char* ws = static_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(ws);
+  a.dq_acc = reinterpret_cast<float*>(ws + round_up((size_t)stat_count(p) * sizeof(float), kAlign));
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool bf = p->dtype == ATTN_BF16;
+  const bool causal = p->causal != 0, det = p->deterministic != 0;
+  const int dt = dtile_for(p->head_dim);
+  const int qblocks = (p->seqlen_q + attn::kPreRows - 1) / attn::kPreRows;
+  const int kblocks = num_kv_splits(p);
+
+  if ((phases & ATTN_PHASE_PREPROCESS) && qblocks > 0) {
+    dim3 grid(qblocks, p->heads_q, p->batch);
+    const int clear = det ? 0 : 1;
+    if (bf) hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<true>), grid, dim3(256), 0, hs, a, clear);
+    else hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<false>), grid, dim3(256), 0, hs, a, clear);
+    if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
+  }
+  if ((phases & ATTN_PHASE_MAIN) && kblocks > 0) {
+    dim3 grid(kblocks, p->heads_kv, p->batch);
+    if (bf) launch_main<true>(a, dt, causal, det, grid, hs);
+    else launch_main<false>(a, dt, causal, det, grid, hs);
+    if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
+  }
+  if ((phases & ATTN_PHASE_POSTPROCESS) && qblocks > 0) {
+    dim3 grid(qblocks, p->heads_q, p->batch);
+    if (bf) launch_post<true>(a, causal, det, grid, hs);
+    else launch_post<false>(a, causal, det, grid, hs);
+    if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes_given, float* delta_out, void* stream) {
+  return attn_bwd_phases(p, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes_given, delta_out,
+                         stream, ATTN_PHASE_ALL);
+}
+
+}  // extern "C"

@@ -1,0 +1,201 @@
+// Attention forward on gfx950: O = softmax(scale * Q K^T, masked) V and the
+// natural-log LSE the backward pass consumes.
+//
+// Method: tilelang test_tilelang_kernel_mha_bwd.py, flashattn_fwd -- one
+// workgroup per (query block, head, batch), an online softmax over key blocks
+// in the exp2 domain with scale*log2(e) folded into one constant, rescaling
+// the running output when the row maximum grows, and the final division by
+// the row sum.  The stored statistic is converted to natural log, the form the
+// flash-attention CK mha_bwd.cpp page's softmax_lse takes.
+//
+// gfx950 design (not the page's): 4 wave64s, each owning 32 query rows; the
+// score tile is computed transposed, S^T = K Q^T, so that every lane holds one
+// query row (its column) -- the row max / row sum need only an in-lane
+// reduction plus one exchange between the two lane halves, and the
+// probabilities P^T leave the MFMA already in the operand layout of
+// O^T += V^T P^T.  V^T is read from the row-major V tile in LDS with the LDS
+// transpose read, so no transposed copy is written.  Q stays in registers for
+// the whole kernel; the next K/V block is prefetched into registers while the
+// current one is used.
+#pragma once
+
+#include "attn_device.h"
+
+namespace attn {
+
+constexpr int kFwdBM = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int kFwdBN = 64;   // key rows per iteration
+
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(Args a) {
+  constexpr int BM = kFwdBM, BN = kFwdBN, LD = D + 8;
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int NCH = BN * CPR / 256;     // chunks per thread per K (or V) block
+  constexpr int TK = BN / 32;             // key tiles per block
+  constexpr int TD = D / 32;              // head-dim tiles
+  static_assert(BN * CPR % 256 == 0, "tile/thread mismatch");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int c32 = lane & 31;
+  const int hq = blockIdx.y;
+  const int z = blockIdx.z;
+  const Seq s = seq_info(a, z);
+  const int qb0 = blockIdx.x * BM;
+  if (qb0 >= s.sq) return;
+  const int g = hq / a.group;
+  const int hd = a.head_dim;
+
+  // This lane's query row (a column of S^T).
+  const int qi = qb0 + 32 * w + c32;
+  const bool q_ok = qi < s.sq;
+
+  // Q as the B operand of S^T = K Q^T: column qi, k = head dim.
+  u32x4 qf[D / 16];
+  {
+    const uint16_t* qp = a.q + s.bq * a.q_b + (int64_t)(s.q0 + qi) * a.q_r + (int64_t)hq * a.q_h;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const int d0 = 16 * st + 8 * h;
+      qf[st] = (q_ok && d0 < hd) ? ldg128(qp + d0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // Key blocks this query block sees.
+  int n_end = (s.sk + BN - 1) / BN;
+  if (CAUSAL) {
+    const int q_last = min(qb0 + BM, s.sq) - 1;
+    const int k_lim = q_last + (s.sk - s.sq);  // last visible key of the block
+    n_end = k_lim < 0 ? 0 : min(n_end, k_lim / BN + 1);
+  }
+
+  const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
+  const uint16_t* vbase = a.v + s.bk * a.v_b + (int64_t)s.k0 * a.v_r + (int64_t)g * a.v_h;
+
+  u32x4 kreg[NCH], vreg[NCH];
+  auto load_kv = [&](int nb) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int id = tid + 256 * i;
+      const int r = id / CPR, c = id % CPR;
+      const int row = nb * BN + r;
+      const bool ok = row < s.sk && 8 * c < hd;
+      kreg[i] = ok ? ldg128(kbase + (int64_t)row * a.k_r + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      vreg[i] = ok ? ldg128(vbase + (int64_t)row * a.v_r + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
+  f32x16 oacc[TD];
+#pragma unroll
+  for (int t = 0; t < TD; ++t) oacc[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int tr_off = tr_lane_offset(lane, LD);
+
+  if (n_end > 0) load_kv(0);
+  for (int nb = 0; nb < n_end; ++nb) {
+    __syncthreads();  // all waves are done with the previous block
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int id = tid + 256 * i;
+      const int r = id / CPR, c = id % CPR;
+      sts128(sK + r * LD + 8 * c, kreg[i]);
+      sts128(sV + r * LD + 8 * c, vreg[i]);
+    }
+    __syncthreads();
+    if (nb + 1 < n_end) load_kv(nb + 1);
+
+    // S^T (keys x queries) for this lane's 32 query columns.
+    f32x16 st[TK];
+#pragma unroll
+    for (int tk = 0; tk < TK; ++tk) {
+      st[tk] = f32x16{};
+#pragma unroll
+      for (int sd = 0; sd < D / 16; ++sd) {
+        const u32x4 af = lds128(sK + (32 * tk + c32) * LD + 16 * sd + 8 * h);
+        st[tk] = mfma32<BF16>(af, qf[sd], st[tk]);
+      }
+    }
+
+    // Scale into the exp2 domain, mask, row max over keys.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tk = 0; tk < TK; ++tk) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kv = nb * BN + 32 * tk + 8 * (j >> 2) + 4 * h + (j & 3);
+        bool vis = kv < s.sk;
+        if (CAUSAL) vis = vis && (kv <= qi + (s.sk - s.sq));
+        const float x = vis ? st[tk][j] * a.scale_log2 : -INFINITY;
+        st[tk][j] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float ls = 0.f;
+#pragma unroll
+    for (int tk = 0; tk < TK; ++tk) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float p = fast_exp2(st[tk][j] - m_use);
+        st[tk][j] = p;
+        ls += p;
+      }
+    }
+    ls += __shfl_xor(ls, 32);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int t = 0; t < TD; ++t) oacc[t] *= alpha;
+
+    // O^T += V^T P^T: P^T leaves the MFMA in B-operand layout (k = keys).
+#pragma unroll
+    for (int tk = 0; tk < TK; ++tk) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 pf;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pf[e] = pack2<BF16>(st[tk][8 * s2 + 2 * e], st[tk][8 * s2 + 2 * e + 1]);
+        const int ra = 32 * tk + 16 * s2 + 4 * h;
+#pragma unroll
+        for (int t = 0; t < TD; ++t) {
+          const u32x4 vf = tr_frag(sV + 32 * t + tr_off, LD, ra, ra + 8);
+          oacc[t] = mfma32<BF16>(vf, pf, oacc[t]);
+        }
+      }
+    }
+  }
+
+  // Normalise and store.  O^T tile: lane column = query qi, rows = head dim in
+  // runs of 4 consecutive elements -> one 8-byte store per run.
+  const float inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+  if (q_ok) {
+    uint16_t* op = a.out_o + s.bq * a.o_b + (int64_t)(s.q0 + qi) * a.o_r + (int64_t)hq * a.o_h;
+#pragma unroll
+    for (int t = 0; t < TD; ++t) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * t + 8 * jj + 4 * h;
+        if (d0 < hd) {
+          u32x2 pk;
+          pk[0] = pack2<BF16>(oacc[t][4 * jj] * inv_l, oacc[t][4 * jj + 1] * inv_l);
+          pk[1] = pack2<BF16>(oacc[t][4 * jj + 2] * inv_l, oacc[t][4 * jj + 3] * inv_l);
+          *reinterpret_cast<u32x2*>(op + d0) = pk;
+        }
+      }
+    }
+    if (h == 0) {
+      const float lse = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : INFINITY;
+      a.lse_out[s.stat0 + (int64_t)hq * s.stat_h + qi] = lse;
+    }
+  }
+}
+
+}  // namespace attn

@@ -1,0 +1,161 @@
+/*
+ * attn.h -- C ABI of libattn.so: FlashAttention-style attention forward and
+ * backward for AMD Instinct MI355X (gfx950).
+ *
+ * The backward pass recomputes the softmax probabilities tile by tile from the
+ * saved log-sum-exp instead of storing them, and produces dQ, dK, dV in three
+ * launches: a preprocess (Delta = rowsum(dO o O), clear of an fp32 dQ
+ * accumulator), a KV-stationary main kernel (five matrix-core contractions,
+ * dQ accumulated in fp32) and a postprocess (dQ = scale * accumulator,
+ * converted to fp16/bf16).  The forward produces O and the LSE the backward
+ * consumes.
+ *
+ * Conventions for every entry point
+ *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent) on
+ *    the device that is current when the call is made.  `stream` is a
+ *    hipStream_t passed as void* (NULL = the null stream).
+ *  - Calls are asynchronous on `stream`; the library never synchronises, never
+ *    allocates device memory, never frees, and keeps no mutable global state.
+ *    Ownership of every buffer stays with the caller.
+ *  - Validation runs on the host before anything is launched; a call that
+ *    returns an error has launched nothing and written nothing.  Faults of
+ *    launched kernels surface at the caller's next synchronisation.
+ *  - Tensors are [batch, seq, heads, head_dim] with element strides given in
+ *    attn_params (last dim contiguous), or, in varlen mode, packed
+ *    [total, heads, head_dim] with batch stride ignored.  Q, O, dO, dQ have
+ *    heads_q heads; K, V, dK, dV have heads_kv heads, and query head h reads
+ *    KV head h / (heads_q / heads_kv) (flash-attention CK mha_bwd.cpp, the
+ *    GQA reshape to [b, s_k, h_k, h/h_k, d] summed over the group axis).
+ *  - LSE is fp32, natural log, contiguous [batch, heads_q, seqlen_q]
+ *    (varlen: [heads_q, total_q]), as the CK mha_bwd.cpp page's softmax_lse
+ *    and the Hopper flash_bwd_launch_template.h page's softmax_lse_ptr take it.
+ *    A query row that sees no key has O = 0 and LSE = +inf.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARGUMENT = 1,   /* bad shape, stride, pointer or flag */
+  ATTN_ERR_UNSUPPORTED = 2,        /* valid for the method, not built here */
+  ATTN_ERR_WORKSPACE_TOO_SMALL = 3,
+  ATTN_ERR_HIP = 4                 /* a HIP runtime call or launch failed */
+} attn_status;
+
+typedef enum { ATTN_FP16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Element strides of a 4-D [batch, seq, head, dim] tensor (dim stride is 1). */
+typedef struct {
+  int64_t batch;
+  int64_t row;
+  int64_t head;
+} attn_strides;
+
+typedef struct {
+  attn_dtype dtype;        /* fp16 or bf16; every tensor has this type
+                              (CK mha_bwd.cpp: q, k, v, out, dout same dtype) */
+  int32_t batch;           /* B > 0, or the number of packed sequences */
+  int32_t seqlen_q;        /* fixed-length Sq (>= 0); varlen: max length */
+  int32_t seqlen_k;        /* fixed-length Sk (>= 0); varlen: max length */
+  int32_t heads_q;         /* H > 0 */
+  int32_t heads_kv;        /* Hk > 0, H % Hk == 0 */
+  int32_t head_dim;        /* d % 8 == 0; d in {64, 96, 128} is built */
+  float softmax_scale;     /* scores are scale * Q K^T; pass 1/sqrt(d) */
+  int32_t causal;          /* 0/1; key j visible to query i iff
+                              j <= i + (Sk - Sq) (bottom-right aligned) */
+  int32_t deterministic;   /* bwd: 1 = dQ bit-identical run to run */
+  const int32_t *cu_seqlens_q;  /* device int32[batch+1] prefix sums, or NULL */
+  const int32_t *cu_seqlens_k;  /* both NULL (fixed length) or both set */
+  int32_t total_q;         /* varlen: cu_seqlens_q[batch] (host copy) */
+  int32_t total_k;         /* varlen: cu_seqlens_k[batch] (host copy) */
+  attn_strides q, k, v, o, dout, dq, dk, dv;
+} attn_params;
+
+/*
+ * Forward: O = softmax(scale * Q K^T, masked) V and LSE (natural log).
+ * tilelang test_tilelang_kernel_mha_bwd.py, flashattn_fwd (online softmax in
+ * the exp2 domain with scale * log2(e) folded into one constant) and
+ * ref_program (the definition).
+ *   q [.., Sq, H, d], k, v [.., Sk, Hk, d]: inputs, read only.
+ *   o [.., Sq, H, d]: output, fully overwritten.
+ *   lse fp32 [B, H, Sq] (varlen [H, total_q]): output, fully overwritten.
+ * Errors: ATTN_ERR_INVALID_ARGUMENT / ATTN_ERR_UNSUPPORTED before any launch;
+ * ATTN_ERR_HIP if a launch fails.
+ */
+attn_status attn_fwd(const attn_params *p, const void *q, const void *k, const void *v,
+                     void *o, float *lse, void *stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for these parameters: Delta
+ * (fp32 [B, H, Sq]) and the fp32 dQ accumulator (one slice, or one slice per
+ * KV block in deterministic mode, as the CK mha_bwd.cpp page sizes dq_accum
+ * with nsplits = ceil(Sk / kN0)).  Never allocates.
+ */
+attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
+
+/*
+ * Backward: dQ, dK, dV of sum(O o dO).
+ *   tilelang flashattn_bwd_preprocess / flashattn_bwd / flashattn_bwd_postprocess;
+ *   flash-attention CK mha_bwd.cpp, mha_bwd (argument contract);
+ *   Hopper flash_bwd_launch_template.h, run_flash_bwd (launch order:
+ *   preprocess, main, dQ postprocess scaled by scale_softmax).
+ *   q, k, v, o, dout, lse: inputs (o, lse from attn_fwd), read only.
+ *   dq [.., Sq, H, d], dk, dv [.., Sk, Hk, d]: outputs, fully overwritten; dK
+ *   and dV of a KV head are summed over the query heads of its group.
+ *   workspace: device buffer of at least attn_bwd_workspace_size() bytes,
+ *   256-byte aligned; its contents on entry do not matter.
+ *   delta_out: NULL, or a device fp32 buffer laid out like lse that receives
+ *   Delta = rowsum(dO o O) (for tests).
+ * In atomic mode (deterministic == 0) dQ is summed with fp32 atomics and its
+ * low-order bits may vary from run to run; deterministic mode writes one
+ * accumulator slice per KV block and sums them in ascending KV-block order.
+ * Sq == 0 gives dK = dV = 0; Sk == 0 gives dQ = 0.
+ * Errors: as attn_fwd, plus ATTN_ERR_WORKSPACE_TOO_SMALL.
+ */
+attn_status attn_bwd(const attn_params *p, const void *q, const void *k, const void *v,
+                     const void *o, const float *lse, const void *dout,
+                     void *dq, void *dk, void *dv,
+                     void *workspace, size_t workspace_bytes,
+                     float *delta_out, void *stream);
+
+/*
+ * The same backward pass, launching only the phases selected in `phases`
+ * (bitwise OR of ATTN_PHASE_*), in the order preprocess, main, postprocess.
+ * attn_bwd == attn_bwd_phases(..., ATTN_PHASE_ALL).  Lets a caller time or
+ * schedule the three kernels separately (the Hopper
+ * flash_bwd_launch_template.h page's run_flash_bwd launches them as three
+ * kernels on one stream).  Phases communicate only through `workspace`: the
+ * main phase reads Delta and (atomic mode) the cleared accumulator the
+ * preprocess left there, the postprocess reads the accumulator; running a
+ * phase without its predecessor on the same workspace gives unspecified (but
+ * finite-memory, in-bounds) results.  Arguments, validation and errors as
+ * attn_bwd; phases == 0 or an unknown bit is ATTN_ERR_INVALID_ARGUMENT.
+ */
+#define ATTN_PHASE_PREPROCESS 1u
+#define ATTN_PHASE_MAIN 2u
+#define ATTN_PHASE_POSTPROCESS 4u
+#define ATTN_PHASE_ALL 7u
+attn_status attn_bwd_phases(const attn_params *p, const void *q, const void *k, const void *v,
+                            const void *o, const float *lse, const void *dout,
+                            void *dq, void *dk, void *dv,
+                            void *workspace, size_t workspace_bytes,
+                            float *delta_out, void *stream, unsigned phases);
+
+/* Static, NUL-terminated description of a status code. */
+const char *attn_status_string(attn_status s);
+
+/* Library build identifier (static string), e.g. for logs. */
+const char *attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */
