@@ -13,7 +13,7 @@
 #include <cstdint>
 #include <cstring>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "attn_bwd.h"
 #include "attn_device.h"
 #include "attn_fwd.h"

@@ -138,9 +138,19 @@ __device__ __forceinline__ uint16_t to_bits(float x) {
   }
 }
 
+// Two fp32 -> one dword of two 16-bit values (round to nearest even), one
+// v_cvt_pk_{bf16,f16}_f32.
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)to_bits<BF16>(lo) | ((uint32_t)to_bits<BF16>(hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  if constexpr (BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  }
 }
 
 template <bool BF16>
@@ -214,6 +224,154 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t* p, int ld, int ra, int 
   r[2] = y[0];
   r[3] = y[1];
   return r;
+}
+
+// ---------------------------------------------------------------------------
+// Buffer resources: range-checked global access.  A raw buffer access whose
+// byte offset lies at or past num_records is dropped (stores, atomics) or
+// reads zero (loads), so tile tails need no branches: rows past the end of a
+// sequence and head-dim columns past head_dim are steered out of range.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // 32-bit data format, raw (untyped) access
+constexpr int kOffOOB = 0x7fffff00;           // an offset past every num_records used
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t num_bytes) {
+  const int n = num_bytes <= 0 ? 0 : (num_bytes >= 0x7fffff00 ? 0x7fffff00 : (int)num_bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buf_load128(rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float buf_load_f32(rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void buf_store_u16(rsrc_t r, int off, uint16_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_store_f32(rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buf_atomic_add_f32(rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads (gfx950 buffer_load ... lds).  Lane t's 16 bytes
+// (or 4 bytes) land at LDS byte address m0 + 16*t (4*t); lanes whose offset
+// is out of range write zeros.  Issued through inline asm so that the
+// compiler does not wait for them before unrelated LDS reads; the caller
+// waits with wait_vmcnt<>() and publishes with lds_barrier().
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// Buffer descriptor in scalar registers for the inline-asm loads.
+__device__ __forceinline__ u32x4 make_srd(const void* base, int64_t num_bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const int n = num_bytes <= 0 ? 0 : (num_bytes >= 0x7fffff00 ? 0x7fffff00 : (int)num_bytes);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)n);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+__device__ __forceinline__ void dma16(u32x4 srd, int off, uint32_t lds_byte) {
+  __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte) : "memory");
+}
+
+__device__ __forceinline__ void dma4(u32x4 srd, int off, uint32_t lds_byte) {
+  __asm__ volatile("buffer_load_dword %0, %1, 0 offen lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte) : "memory");
+}
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ u32x4 lds_rd128(const uint8_t* base, int byte_off) {
+  return *reinterpret_cast<const u32x4*>(base + byte_off);
+}
+
+__device__ __forceinline__ u32x4 tr_frag_b(const uint8_t* base, int off_a, int off_b) {
+  const u32x2 x = lds_tr4(reinterpret_cast<const uint16_t*>(base + off_a));
+  const u32x2 y = lds_tr4(reinterpret_cast<const uint16_t*>(base + off_b));
+  u32x4 r;
+  r[0] = x[0];
+  r[1] = x[1];
+  r[2] = y[0];
+  r[3] = y[1];
+  return r;
+}
+
+// Workgroup barrier for LDS hand-off: wait for this wave's LDS reads/writes,
+// then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
+// global memory operations (the dQ atomics stay in flight); a caller that
+// published data with direct global->LDS loads waits for them first with
+// wait_vmcnt<>().  The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wave index as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// ---------------------------------------------------------------------------
+// Instruction-scheduling hints (sched_group_barrier masks: 0x8 MFMA,
+// 0x100 DS read, 0x200 DS write, 0x2 VALU).  pipeline_hint<N, R, A>() asks the
+// scheduler to issue, for a straight-line section of N MFMAs each fed by R LDS
+// reads, the reads A MFMAs ahead of their use, so the matrix core does not
+// wait for each read's latency.  Placed at the end of the section.
+// ---------------------------------------------------------------------------
+template <int N, int R, int A>
+__device__ __forceinline__ void pipeline_hint() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R * A, 0);
+#pragma unroll
+  for (int i = 0; i < N - A; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < A; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+
+// ---------------------------------------------------------------------------
+// LDS tile swizzle.  Tiles are row-major with rows of CPR 16-byte chunks;
+// chunk c of row r is stored at chunk position c ^ swz(r).  Chosen so that
+// the three access patterns of the kernels -- 16 lanes reading 16 consecutive
+// rows at one chunk (ds_read_b128), and 32 lanes transposing a 4-row x
+// 32-column block from each of two 4-row groups (ds_read_b64_tr_b16) -- each
+// touch every bank once (64 banks x 4 bytes).
+// ---------------------------------------------------------------------------
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(CPR == 8 || CPR == 16, "rows of 128 or 256 bytes");
+  if constexpr (CPR == 16) {
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  } else {
+    return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+}
+
+// Byte offset of element column `col` (16-bit elements) of row r.
+template <int CPR>
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * CPR * 16 + (((col >> 3) ^ swz<CPR>(r)) << 4) + ((col & 7) << 1);
 }
 
 }  // namespace attn
