@@ -37,9 +37,13 @@ import workloads  # noqa: E402
 
 MFMA_PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = ["flashattention_backward_pass_attn_amd/csrc/attn_bwd.h",
+KERNEL_SOURCES = ["flashattention_backward_pass_attn_amd/csrc/attn_bwd_split.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_device.h"]
-TRAFFIC_FILE = "profiles/bwd_main_traffic_{workload}.json"
+TRAFFIC_FILE = "profiles/bwd_{kernel}_traffic_{workload}.json"
+# Matrix-core work of each gradient kernel, in units of 2*b*h*Sq*Sk*d (halved
+# when causal): dK/dV does S, dP, dV, dK; dQ does S, dP, dQ.  The metric counts
+# the method's 5 contractions (10*b*h*Sq*Sk*d) for the whole backward.
+KERNEL_UNITS = {"attn_bwd_dkdv_kernel": 4, "attn_bwd_dq_kernel": 3}
 
 
 def log(*a):
@@ -61,8 +65,8 @@ def workload_flops(w: workloads.Workload, inp) -> float:
     return workloads.attention_flops(w.batch, w.heads_q, w.seqlen, w.seqlen, w.head_dim, w.causal)
 
 
-def load_traffic(workload: str):
-    path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
+def load_traffic(workload: str, kernel: str):
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload, kernel=kernel))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -183,17 +187,17 @@ def main(argv=None):
         e[0].record()
         fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_PREPROCESS, **common)
         e[1].record()
-        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_MAIN, **common)
+        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_DKDV, **common)
         e[2].record()
-        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_POSTPROCESS, **common)
+        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_DQ, **common)
         e[3].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
     pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    main_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    post_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
-    log(f"{w.name}: step {ms_per_step:.4f} ms (events: pre {pre_ms:.4f} main {main_ms:.4f} post {post_ms:.4f} ms)")
+    dkdv_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
+    dq_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
+    log(f"{w.name}: step {ms_per_step:.4f} ms (events: pre {pre_ms:.4f} dkdv {dkdv_ms:.4f} dq {dq_ms:.4f} ms)")
 
     if args.copy_calibration:
         n = 1 << 28  # 256 Mi floats = 1 GiB read + 1 GiB written
@@ -205,20 +209,26 @@ def main(argv=None):
         log(f"copy calibration: {n * 4} bytes read and written per copy kernel, 2 launches")
 
     tflops = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (main_ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic(w.name)
+    kernels = {"attn_bwd_dkdv_kernel": dkdv_ms, "attn_bwd_dq_kernel": dq_ms}
+    per_kernel = {}
+    for name, ms in kernels.items():
+        kfl = flops / 5.0 * KERNEL_UNITS[name]
+        per_kernel[name] = {"ms": round(ms, 4), "tflops": round(kfl / (ms * 1e-3) / 1e12, 2),
+                            "frac": round(kfl / (ms * 1e-3) / 1e12 / peak, 4), "flop": kfl}
+    dom = max(kernels, key=kernels.get)
+    traffic = load_traffic(w.name, dom.replace("attn_bwd_", "").replace("_kernel", ""))
     roofline = {
         "bound": "mfma",
-        "achieved": round(achieved, 2),
+        "achieved": per_kernel[dom]["tflops"],
         "peak": peak,
         "unit": "TFLOP/s",
-        "frac": round(achieved / peak, 4),
+        "frac": per_kernel[dom]["frac"],
         "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
-        "kernel": "attn_bwd_main_kernel",
-        "kernel_ms": round(main_ms, 4),
+        "kernel": dom,
+        "kernel_ms": per_kernel[dom]["ms"],
+        "kernels": per_kernel,
         "preprocess_ms": round(pre_ms, 4),
-        "postprocess_ms": round(post_ms, 4),
     }
     cpu = None
     if args.cpu_baseline_seconds > 0:

@@ -26,8 +26,8 @@ ATTN_BF16 = 1
 EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_phases", "attn_status_string",
                     "attn_version")
 PHASE_PREPROCESS = 1
-PHASE_MAIN = 2
-PHASE_POSTPROCESS = 4
+PHASE_DKDV = 2
+PHASE_DQ = 4
 PHASE_ALL = 7
 
 

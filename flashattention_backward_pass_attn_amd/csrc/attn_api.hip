@@ -6,7 +6,10 @@
 // batch > 0; head_dim % 8 == 0 and <= 256; heads_q % heads_kv == 0), returning
 // a status code instead of throwing.  Nothing is launched unless every check
 // passes.  Launch order follows the Hopper flash_bwd_launch_template.h page's
-// run_flash_bwd: preprocess, main, dQ postprocess, all on the caller's stream.
+// run_flash_bwd: the preprocess first, then the gradient kernels, all on the
+// caller's stream.  Here the gradients come from two kernels (dK/dV
+// KV-stationary, dQ Q-stationary) instead of one kernel with fp32 dQ atomics
+// plus a dQ postprocess; see attn_bwd_split.h for why.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -15,6 +18,7 @@
 
 #include "attn.h"
 #include "attn_bwd.h"
+#include "attn_bwd_split.h"
 #include "attn_device.h"
 #include "attn_fwd.h"
 
@@ -66,15 +70,8 @@ int64_t stat_count(const attn_params* p) {
                       : (int64_t)p->batch * p->heads_q * p->seqlen_q;
 }
 
-int num_kv_splits(const attn_params* p) { return (p->seqlen_k + attn::kBwdBN - 1) / attn::kBwdBN; }
-
-size_t acc_elems(const attn_params* p) { return (size_t)stat_count(p) * (size_t)p->head_dim; }
-
 size_t workspace_bytes(const attn_params* p) {
-  const size_t delta = round_up((size_t)stat_count(p) * sizeof(float), kAlign);
-  const size_t splits = p->deterministic ? (size_t)std::max(num_kv_splits(p), 1) : 1;
-  const size_t acc = round_up(splits * acc_elems(p) * sizeof(float), kAlign);
-  return delta + acc;
+  return round_up((size_t)stat_count(p) * sizeof(float), kAlign);
 }
 
 Args make_args(const attn_params* p) {
@@ -107,7 +104,6 @@ Args make_args(const attn_params* p) {
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * attn::kLog2e;
   a.varlen = vl ? 1 : 0;
-  a.acc_split = (int64_t)acc_elems(p);
   return a;
 }
 
@@ -132,34 +128,29 @@ void launch_fwd(const Args& a, int dtile, bool causal, dim3 grid, hipStream_t st
     launch_fwd_d<BF16, 128>(a, causal, grid, st);
 }
 
-template <bool BF16, int D, bool CAUSAL>
-void launch_main_c(const Args& a, bool det, dim3 grid, hipStream_t st) {
-  if (det)
-    hipLaunchKernelGGL((attn::attn_bwd_main_kernel<BF16, D, CAUSAL, true>), grid, dim3(256), 0, st, a);
+template <bool BF16, int D>
+void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q, hipStream_t st) {
+  if (phases & ATTN_PHASE_DKDV) {
+    if (causal)
+      hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, true>), grid_kv, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, false>), grid_kv, dim3(512), 0, st, a);
+  }
+  if (phases & ATTN_PHASE_DQ) {
+    if (causal)
+      hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, true>), grid_q, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, false>), grid_q, dim3(512), 0, st, a);
+  }
+}
+
+template <bool BF16>
+void launch_grads(const Args& a, int dtile, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q,
+                  hipStream_t st) {
+  if (dtile == 64)
+    launch_grads_d<BF16, 64>(a, causal, phases, grid_kv, grid_q, st);
   else
-    hipLaunchKernelGGL((attn::attn_bwd_main_kernel<BF16, D, CAUSAL, false>), grid, dim3(256), 0, st, a);
-}
-
-template <bool BF16>
-void launch_main(const Args& a, int dtile, bool causal, bool det, dim3 grid, hipStream_t st) {
-  if (dtile == 64) {
-    if (causal) launch_main_c<BF16, 64, true>(a, det, grid, st);
-    else launch_main_c<BF16, 64, false>(a, det, grid, st);
-  } else {
-    if (causal) launch_main_c<BF16, 128, true>(a, det, grid, st);
-    else launch_main_c<BF16, 128, false>(a, det, grid, st);
-  }
-}
-
-template <bool BF16>
-void launch_post(const Args& a, bool causal, bool det, dim3 grid, hipStream_t st) {
-  if (det) {
-    if (causal) hipLaunchKernelGGL((attn::attn_bwd_post_kernel<BF16, true, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn::attn_bwd_post_kernel<BF16, false, true>), grid, dim3(256), 0, st, a);
-  } else {
-    if (causal) hipLaunchKernelGGL((attn::attn_bwd_post_kernel<BF16, true, false>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((attn::attn_bwd_post_kernel<BF16, false, false>), grid, dim3(256), 0, st, a);
-  }
+    launch_grads_d<BF16, 128>(a, causal, phases, grid_kv, grid_q, st);
 }
 
 int dtile_for(int head_dim) { return head_dim <= 64 ? 64 : 128; }
@@ -245,34 +236,30 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   a.dv = static_cast<uint16_t*>(dv);
   a.lse_in = lse;
   a.delta_out = delta_out;
-  char* ws = static_cast<char*>(workspace);
-  a.delta = reinterpret_cast<float*>(ws);
-  a.dq_acc = reinterpret_cast<float*>(ws + round_up((size_t)stat_count(p) * sizeof(float), kAlign));
+  a.delta = static_cast<float*>(workspace);
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool bf = p->dtype == ATTN_BF16;
-  const bool causal = p->causal != 0, det = p->deterministic != 0;
+  const bool causal = p->causal != 0;
   const int dt = dtile_for(p->head_dim);
   const int qblocks = (p->seqlen_q + attn::kPreRows - 1) / attn::kPreRows;
-  const int kblocks = num_kv_splits(p);
 
   if ((phases & ATTN_PHASE_PREPROCESS) && qblocks > 0) {
     dim3 grid(qblocks, p->heads_q, p->batch);
-    const int clear = det ? 0 : 1;
-    if (bf) hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<true>), grid, dim3(256), 0, hs, a, clear);
-    else hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<false>), grid, dim3(256), 0, hs, a, clear);
+    if (bf) hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<true>), grid, dim3(256), 0, hs, a);
+    else hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<false>), grid, dim3(256), 0, hs, a);
     if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
   }
-  if ((phases & ATTN_PHASE_MAIN) && kblocks > 0) {
-    dim3 grid(kblocks, p->heads_kv, p->batch);
-    if (bf) launch_main<true>(a, dt, causal, det, grid, hs);
-    else launch_main<false>(a, dt, causal, det, grid, hs);
-    if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
-  }
-  if ((phases & ATTN_PHASE_POSTPROCESS) && qblocks > 0) {
-    dim3 grid(qblocks, p->heads_q, p->batch);
-    if (bf) launch_post<true>(a, causal, det, grid, hs);
-    else launch_post<false>(a, causal, det, grid, hs);
+  unsigned grad_phases = phases & (ATTN_PHASE_DKDV | ATTN_PHASE_DQ);
+  const int kvblocks = (p->seqlen_k + attn::kDkvBN - 1) / attn::kDkvBN;
+  const int dqblocks = (p->seqlen_q + attn::kDqBM - 1) / attn::kDqBM;
+  if (kvblocks == 0) grad_phases &= ~ATTN_PHASE_DKDV;  // no keys: nothing to write in dK/dV
+  if (dqblocks == 0) grad_phases &= ~ATTN_PHASE_DQ;    // no queries: no dQ rows
+  if (grad_phases) {
+    dim3 grid_kv(kvblocks > 0 ? kvblocks : 1, p->heads_kv, p->batch);
+    dim3 grid_q(dqblocks > 0 ? dqblocks : 1, p->heads_q, p->batch);
+    if (bf) launch_grads<true>(a, dt, causal, grad_phases, grid_kv, grid_q, hs);
+    else launch_grads<false>(a, dt, causal, grad_phases, grid_kv, grid_q, hs);
     if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
   }
   return ATTN_OK;

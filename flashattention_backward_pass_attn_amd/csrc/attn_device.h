@@ -46,7 +46,6 @@ struct Args {
   float* lse_out;       // forward output (natural log)
   float* delta;         // workspace, laid out like lse
   float* delta_out;     // optional copy of delta
-  float* dq_acc;        // workspace, fp32
   const int32_t* cu_q;
   const int32_t* cu_k;
   // element strides: batch, row, head (dim stride is 1)
@@ -58,9 +57,8 @@ struct Args {
   int64_t dq_b, dq_r, dq_h;
   int64_t dk_b, dk_r, dk_h;
   int64_t dv_b, dv_r, dv_h;
-  int64_t acc_split;  // elements between deterministic dQ accumulator slices
   int32_t batch, seqlen_q, seqlen_k, heads_q, heads_kv, group, head_dim;
-  int32_t total_q;  // varlen: packed rows (stat/accumulator row count per head)
+  int32_t total_q;  // varlen: packed rows (row count per head of LSE / Delta)
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   int32_t varlen;
@@ -97,12 +95,6 @@ __device__ inline Seq seq_info(const Args& a, int z) {
     s.stat_h = a.seqlen_q;
   }
   return s;
-}
-
-// Offset (elements) of row 0, head h of the dQ accumulator for sequence z.
-// Layout: fixed [B][H][Sq][d], varlen [H][total_q][d] (d = head_dim).
-__device__ inline int64_t acc_base(const Args& a, const Seq& s, int h) {
-  return (s.stat0 + (int64_t)h * s.stat_h) * a.head_dim;
 }
 
 // First q block (of BM rows) that sees any key of KV block n (of BN rows).

@@ -4,10 +4,9 @@
  *
  * The backward pass recomputes the softmax probabilities tile by tile from the
  * saved log-sum-exp instead of storing them, and produces dQ, dK, dV in three
- * launches: a preprocess (Delta = rowsum(dO o O), clear of an fp32 dQ
- * accumulator), a KV-stationary main kernel (five matrix-core contractions,
- * dQ accumulated in fp32) and a postprocess (dQ = scale * accumulator,
- * converted to fp16/bf16).  The forward produces O and the LSE the backward
+ * launches: a preprocess (Delta = rowsum(dO o O)), a KV-stationary kernel for
+ * dK and dV and a Q-stationary kernel for dQ (matrix-core contractions with
+ * fp32 accumulation).  The forward produces O and the LSE the backward
  * consumes.
  *
  * Conventions for every entry point
@@ -70,7 +69,8 @@ typedef struct {
   float softmax_scale;     /* scores are scale * Q K^T; pass 1/sqrt(d) */
   int32_t causal;          /* 0/1; key j visible to query i iff
                               j <= i + (Sk - Sq) (bottom-right aligned) */
-  int32_t deterministic;   /* bwd: 1 = dQ bit-identical run to run */
+  int32_t deterministic;   /* bwd: 1 = bit-identical run to run (always
+                              satisfied: no atomics are used) */
   const int32_t *cu_seqlens_q;  /* device int32[batch+1] prefix sums, or NULL */
   const int32_t *cu_seqlens_k;  /* both NULL (fixed length) or both set */
   int32_t total_q;         /* varlen: cu_seqlens_q[batch] (host copy) */
@@ -93,19 +93,19 @@ attn_status attn_fwd(const attn_params *p, const void *q, const void *k, const v
                      void *o, float *lse, void *stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these parameters: Delta
- * (fp32 [B, H, Sq]) and the fp32 dQ accumulator (one slice, or one slice per
- * KV block in deterministic mode, as the CK mha_bwd.cpp page sizes dq_accum
- * with nsplits = ceil(Sk / kN0)).  Never allocates.
+ * Bytes of device workspace attn_bwd needs for these parameters: Delta, fp32
+ * laid out like lse (the flash-attention CK mha_bwd.cpp page's softmax_d),
+ * rounded up to 256 bytes.  Never allocates.
  */
 attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
 
 /*
  * Backward: dQ, dK, dV of sum(O o dO).
- *   tilelang flashattn_bwd_preprocess / flashattn_bwd / flashattn_bwd_postprocess;
- *   flash-attention CK mha_bwd.cpp, mha_bwd (argument contract);
- *   Hopper flash_bwd_launch_template.h, run_flash_bwd (launch order:
- *   preprocess, main, dQ postprocess scaled by scale_softmax).
+ *   tilelang test_tilelang_kernel_mha_bwd.py, flashattn_bwd_preprocess and
+ *   flashattn_bwd (the method: P recomputed tile by tile from LSE,
+ *   dS = P o (dP - Delta)); flash-attention CK mha_bwd.cpp, mha_bwd (argument
+ *   contract); Hopper flash_bwd_launch_template.h, run_flash_bwd (preprocess
+ *   first, dQ scaled by scale_softmax).
  *   q, k, v, o, dout, lse: inputs (o, lse from attn_fwd), read only.
  *   dq [.., Sq, H, d], dk, dv [.., Sk, Hk, d]: outputs, fully overwritten; dK
  *   and dV of a KV head are summed over the query heads of its group.
@@ -113,9 +113,11 @@ attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
  *   256-byte aligned; its contents on entry do not matter.
  *   delta_out: NULL, or a device fp32 buffer laid out like lse that receives
  *   Delta = rowsum(dO o O) (for tests).
- * In atomic mode (deterministic == 0) dQ is summed with fp32 atomics and its
- * low-order bits may vary from run to run; deterministic mode writes one
- * accumulator slice per KV block and sums them in ascending KV-block order.
+ * Three launches on `stream`: the preprocess (Delta), a KV-stationary kernel
+ * for dK and dV, and a Q-stationary kernel for dQ that sums the key blocks in
+ * ascending order in registers.  No atomics are used, so every output is
+ * bit-identical from run to run; `deterministic` is accepted and always
+ * satisfied.
  * Sq == 0 gives dK = dV = 0; Sk == 0 gives dQ = 0.
  * Errors: as attn_fwd, plus ATTN_ERR_WORKSPACE_TOO_SMALL.
  */
@@ -126,21 +128,18 @@ attn_status attn_bwd(const attn_params *p, const void *q, const void *k, const v
                      float *delta_out, void *stream);
 
 /*
- * The same backward pass, launching only the phases selected in `phases`
- * (bitwise OR of ATTN_PHASE_*), in the order preprocess, main, postprocess.
+ * The same backward pass, launching only the kernels selected in `phases`
+ * (bitwise OR of ATTN_PHASE_*): the preprocess, then dK/dV, then dQ.
  * attn_bwd == attn_bwd_phases(..., ATTN_PHASE_ALL).  Lets a caller time or
- * schedule the three kernels separately (the Hopper
- * flash_bwd_launch_template.h page's run_flash_bwd launches them as three
- * kernels on one stream).  Phases communicate only through `workspace`: the
- * main phase reads Delta and (atomic mode) the cleared accumulator the
- * preprocess left there, the postprocess reads the accumulator; running a
- * phase without its predecessor on the same workspace gives unspecified (but
- * finite-memory, in-bounds) results.  Arguments, validation and errors as
+ * schedule the kernels separately.  The dK/dV and dQ kernels read Delta from
+ * `workspace`, which the preprocess writes; they do not depend on each other.
+ * Running a gradient phase without a preprocess on the same workspace gives
+ * unspecified (but in-bounds) results.  Arguments, validation and errors as
  * attn_bwd; phases == 0 or an unknown bit is ATTN_ERR_INVALID_ARGUMENT.
  */
 #define ATTN_PHASE_PREPROCESS 1u
-#define ATTN_PHASE_MAIN 2u
-#define ATTN_PHASE_POSTPROCESS 4u
+#define ATTN_PHASE_DKDV 2u
+#define ATTN_PHASE_DQ 4u
 #define ATTN_PHASE_ALL 7u
 attn_status attn_bwd_phases(const attn_params *p, const void *q, const void *k, const void *v,
                             const void *o, const float *lse, const void *dout,
