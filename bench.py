@@ -124,6 +124,59 @@ def cpu_baseline(w: workloads.Workload, inp, budget_s: float):
     }
 
 
+COPY_BYTES = 1 << 30  # the --copy-calibration copy: 1 GiB read and 1 GiB written per launch
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _counter_rows(path: str, counter: str):
+    import csv
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                # "void ns::name<targs>(args)" -> "name"
+                name = r["Kernel_Name"].split("(")[0].split("<")[0].split()[-1].split("::")[-1]
+                rows.setdefault(name, []).append(float(r["Counter_Value"]))
+    return rows
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str, command: str) -> int:
+    """Turn two rocprofv3 --pmc runs of `bench.py --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, both
+    in KiB per dispatch) into per-launch HBM bytes for each gradient kernel.  Each counter is scaled by
+    what it reads for a plain 1 GiB device copy in the same run."""
+    fetch, write = _counter_rows(fetch_csv, "FETCH_SIZE"), _counter_rows(write_csv, "WRITE_SIZE")
+    if COPY_KERNEL not in fetch or COPY_KERNEL not in write:
+        log(f"no {COPY_KERNEL} rows: run the profiled bench with --copy-calibration")
+        return 1
+    f_factor = COPY_BYTES / (sum(fetch[COPY_KERNEL]) / len(fetch[COPY_KERNEL]) * 1024)
+    w_factor = COPY_BYTES / (sum(write[COPY_KERNEL]) / len(write[COPY_KERNEL]) * 1024)
+    for kernel in KERNEL_UNITS:
+        if kernel not in fetch or kernel not in write:
+            log(f"{kernel}: missing from the counter files")
+            return 1
+        fk = sum(fetch[kernel]) / len(fetch[kernel])
+        wk = sum(write[kernel]) / len(write[kernel])
+        rec = {
+            "workload": workload, "kernel": kernel, "source_sha256": kernel_source_sha(),
+            "command": command,
+            "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+            "dispatches": [len(fetch[kernel]), len(write[kernel])],
+            "copy_fetch_factor": round(f_factor, 4), "copy_write_factor": round(w_factor, 4),
+            "hbm_read_bytes_per_launch": round(fk * 1024 * f_factor),
+            "hbm_write_bytes_per_launch": round(wk * 1024 * w_factor),
+        }
+        rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+        short = kernel.replace("attn_bwd_", "").replace("_kernel", "")
+        out = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload, kernel=short))
+        os.makedirs(os.path.dirname(out), exist_ok=True)
+        with open(out, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        log(f"{out}: {rec['hbm_bytes_per_launch'] / 1e9:.3f} GB per launch "
+            f"(factors fetch {f_factor:.3f}, write {w_factor:.3f})")
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,8 +188,15 @@ def main(argv=None):
                     help="CPU time budget of the oracle sample (0 disables the cpu_baseline leg)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the per-launch HBM traffic records from two rocprofv3 --pmc counter_collection "
+                         "files (FETCH_SIZE, WRITE_SIZE) of `bench.py --copy-calibration`, then exit")
+    ap.add_argument("--traffic-command", default="",
+                    help="with --traffic-from: the profiled command, stored in the record")
     args = ap.parse_args(argv)
 
+    if args.traffic_from:
+        return write_traffic(args.traffic_from[0], args.traffic_from[1], args.workload, args.traffic_command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the backward is independent "
               "per (batch, head), so more GPUs would each run this same kernel on their share; no "

@@ -17,7 +17,7 @@ The log-sum-exp the forward hands to the backward is returned in natural-log
 units, as the CK ``mha_bwd.cpp`` page's ``softmax_lse`` argument and the
 Hopper ``flash_bwd_launch_template.h`` page's ``softmax_lse_ptr`` (with a
 separate log2 copy) take it.  The tilelang page stores a log2-domain value
-instead; the two differ by the factor log2(e), see the design doc.
+instead; the two differ by the factor log2(e).
 
 Backward -- the exact gradient of the forward.  Its steps, as the tilelang
 page's ``flashattn_bwd`` kernel lays them out per tile (here evaluated densely,
@@ -43,7 +43,7 @@ Varlen -- packed ``[total, h, d]`` tensors with ``cu_seqlens`` prefix sums
 len(cu_seqlens) - 1``); every sequence is an independent attention problem.
 LSE and Delta are ``[h, total_q]``.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * causal alignment when Sq != Sk is bottom-right: key j is visible to
     query i iff ``j <= i + (Sk - Sq)`` (identical to the tilelang page's
     ``q >= k`` when Sq == Sk);
