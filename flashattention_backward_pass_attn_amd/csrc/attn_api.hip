@@ -138,9 +138,9 @@ void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, d
   }
   if (phases & ATTN_PHASE_DQ) {
     if (causal)
-      hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, true>), grid_q, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, true>), grid_q, dim3(64 * attn::kDqWaves), 0, st, a);
     else
-      hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, false>), grid_q, dim3(512), 0, st, a);
+      hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, false>), grid_q, dim3(64 * attn::kDqWaves), 0, st, a);
   }
 }
 
