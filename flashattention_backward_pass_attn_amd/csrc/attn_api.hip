@@ -55,7 +55,10 @@ attn_status validate_common(const attn_params* p) {
   const bool vq = p->cu_seqlens_q != nullptr, vk = p->cu_seqlens_k != nullptr;
   if (vq != vk) return ATTN_ERR_INVALID_ARGUMENT;
   if (vq && (p->total_q < 0 || p->total_k < 0)) return ATTN_ERR_INVALID_ARGUMENT;
+  // launch-grid limits: head x sequence in grid x, blocks of >= 64 rows in grid y/x
   if (p->heads_q > 65535 || p->batch > 65535) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)p->heads_q * p->batch > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
+  if (p->seqlen_q > 65535 * 64 || p->seqlen_k > 65535 * 64) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -256,8 +259,10 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   if (kvblocks == 0) grad_phases &= ~ATTN_PHASE_DKDV;  // no keys: nothing to write in dK/dV
   if (dqblocks == 0) grad_phases &= ~ATTN_PHASE_DQ;    // no queries: no dQ rows
   if (grad_phases) {
-    dim3 grid_kv(kvblocks > 0 ? kvblocks : 1, p->heads_kv, p->batch);
-    dim3 grid_q(dqblocks > 0 ? dqblocks : 1, p->heads_q, p->batch);
+    // (head x sequence, block): block index slowest, so the longest causal
+    // blocks of every head start first and one head's blocks share an XCD.
+    dim3 grid_kv(p->heads_kv * p->batch, kvblocks > 0 ? kvblocks : 1, 1);
+    dim3 grid_q(p->heads_q * p->batch, dqblocks > 0 ? dqblocks : 1, 1);
     if (bf) launch_grads<true>(a, dt, causal, grad_phases, grid_kv, grid_q, hs);
     else launch_grads<false>(a, dt, causal, grad_phases, grid_kv, grid_q, hs);
     if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;

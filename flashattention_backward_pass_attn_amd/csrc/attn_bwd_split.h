@@ -75,9 +75,12 @@ void attn_bwd_dkdv_kernel(Args a) {
   const int gg = lane >> 4;
   const int rr = sl >> 2;
   const int tcol = 16 * (gg & 1) + 4 * (sl & 3);
-  const int nb = blockIdx.x;
-  const int g = blockIdx.y;
-  const int z = blockIdx.z;
+  // grid (KV head x sequence, key block): every (head, sequence) pair's
+  // blocks of one index go out together, longest (first key block, when
+  // causal) first; the blocks of one pair share an XCD and its L2.
+  const int nb = blockIdx.y;
+  const int g = blockIdx.x % a.heads_kv;
+  const int z = blockIdx.x / a.heads_kv;
   const Seq s = seq_info(a, z);
   const int kv0 = nb * BN;
   if (kv0 >= s.sk) return;
@@ -412,11 +415,12 @@ void attn_bwd_dq_kernel(Args a) {
   const int gg = lane >> 4;
   const int rr = sl >> 2;
   const int tcol = 16 * (gg & 1) + 4 * (sl & 3);
-  const int hq = blockIdx.y;
-  const int z = blockIdx.z;
+  // grid (query head x sequence, query block), as in the dK/dV kernel.
+  const int hq = blockIdx.x % a.heads_q;
+  const int z = blockIdx.x / a.heads_q;
   const Seq s = seq_info(a, z);
   // Causal blocks near the end of a sequence see the most keys: run them first.
-  const int mb = CAUSAL ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+  const int mb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int q0 = mb * BM;
   if (q0 >= s.sq) return;
   const int hd = a.head_dim;
