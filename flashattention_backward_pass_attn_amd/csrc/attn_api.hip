@@ -18,6 +18,7 @@
 
 #include "attn.h"
 #include "attn_bwd.h"
+#include "attn_bwd_dq.h"
 #include "attn_bwd_split.h"
 #include "attn_device.h"
 #include "attn_fwd.h"
@@ -73,9 +74,28 @@ int64_t stat_count(const attn_params* p) {
                       : (int64_t)p->batch * p->heads_q * p->seqlen_q;
 }
 
-size_t workspace_bytes(const attn_params* p) {
+size_t delta_bytes(const attn_params* p) {
   return round_up((size_t)stat_count(p) * sizeof(float), kAlign);
 }
+
+// dS^T chunk grid (see Args::ds): 4 key-tile slots per 128-key block of each
+// sequence plus 4 per sequence for the ragged blocks, and query tiles in
+// pairs (the dK/dV kernel writes 64-query tiles).
+int64_t ds_nkt(const attn_params* p) {
+  const int64_t rows_k = is_varlen(p) ? (int64_t)p->total_k : (int64_t)p->batch * p->seqlen_k;
+  return 4 * (rows_k / 128) + 4 * (int64_t)p->batch + 4;
+}
+int32_t ds_nqt(const attn_params* p) { return 2 * ((p->seqlen_q + 63) / 64); }
+
+size_t ds_bytes(const attn_params* p) {
+  return round_up((size_t)p->heads_q * (size_t)ds_nkt(p) * (size_t)ds_nqt(p) * 2048u, kAlign);
+}
+
+// Full workspace: Delta then the dS^T chunks (the dQ kernel is then a plain
+// product over them).  Minimal workspace: Delta only (the dQ kernel then
+// recomputes dS).
+size_t workspace_bytes(const attn_params* p) { return delta_bytes(p) + ds_bytes(p); }
+size_t workspace_bytes_min(const attn_params* p) { return delta_bytes(p); }
 
 Args make_args(const attn_params* p) {
   Args a;
@@ -140,10 +160,18 @@ void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, d
       hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, false>), grid_kv, dim3(512), 0, st, a);
   }
   if (phases & ATTN_PHASE_DQ) {
-    if (causal)
-      hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, true>), grid_q, dim3(64 * attn::kDqWaves), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, false>), grid_q, dim3(64 * attn::kDqWaves), 0, st, a);
+    const dim3 blk(64 * attn::kDqWaves);
+    if (a.ds != nullptr) {  // dS^T written by the dK/dV kernel: plain product
+      if (causal)
+        hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, true>), grid_q, blk, 0, st, a);
+      else
+        hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, false>), grid_q, blk, 0, st, a);
+    } else {  // minimal workspace: recompute dS
+      if (causal)
+        hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, true>), grid_q, blk, 0, st, a);
+      else
+        hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, false>), grid_q, blk, 0, st, a);
+    }
   }
 }
 
@@ -208,6 +236,14 @@ attn_status attn_bwd_workspace_size(const attn_params* p, size_t* bytes) {
   return ATTN_OK;
 }
 
+attn_status attn_bwd_workspace_size_min(const attn_params* p, size_t* bytes) {
+  attn_status st = validate_common(p);
+  if (st != ATTN_OK) return st;
+  if (!bytes) return ATTN_ERR_INVALID_ARGUMENT;
+  *bytes = workspace_bytes_min(p);
+  return ATTN_OK;
+}
+
 attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, const void* v,
                             const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes_given, float* delta_out, void* stream,
@@ -226,7 +262,8 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return ATTN_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return ATTN_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes_given < workspace_bytes(p)) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes_given < workspace_bytes_min(p)) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  const bool use_ds = workspace_bytes_given >= workspace_bytes(p);
 
   Args a = make_args(p);
   a.q = static_cast<const uint16_t*>(q);
@@ -240,6 +277,12 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   a.lse_in = lse;
   a.delta_out = delta_out;
   a.delta = static_cast<float*>(workspace);
+  if (use_ds) {
+    a.ds = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + delta_bytes(p));
+    a.ds_bytes = (int64_t)ds_bytes(p);
+    a.ds_nkt = ds_nkt(p);
+    a.ds_nqt = ds_nqt(p);
+  }
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool bf = p->dtype == ATTN_BF16;

@@ -1,0 +1,559 @@
+// Attention backward on gfx950: the dQ kernel.
+//
+// dQ = scale * dS K (tilelang test_tilelang_kernel_mha_bwd.py, flashattn_bwd:
+// the dQ contribution of each key block is dS K; the Hopper
+// flash_bwd_launch_template.h page applies the softmax scale to dQ after the
+// sum over key blocks).  dS = P o (dP - Delta) is not recomputed here: the
+// dK/dV kernel, which forms it anyway, writes it to the workspace as bf16 /
+// fp16 dS^T chunks (32 keys x 32 queries, 2 KiB, rows = keys, 64 bytes per
+// row holding query runs 4h + 8r .. +3 at byte 32h + 8r), and this kernel
+// is a plain matrix product over them, summed over key blocks in ascending
+// order in registers -- no atomics, so the result is deterministic.
+//
+// Work: one workgroup per (query head x sequence, 256-query block), 8 waves,
+// wave w owning queries 32w .. +32 of the block.  Each 64-key tile brings
+// the block's dS^T chunks (2 key tiles x 8 query tiles, 32 KiB) and the K
+// tile (swizzled like the other kernels' K tiles) into LDS by direct
+// global->LDS loads, two tiles ahead in three stages; the kernel streams the
+// dS workspace from HBM and is bound by that read.  Per 16-key step the dS
+// A operand (query rows, keys as k) and the K B operand (keys as k,
+// head-dim columns) are both transpose reads, which apply the same key
+// permutation to both operands.  Chunks a wave's queries cannot see (above
+// its causal diagonal or past the last key) were never written: their A
+// operand is replaced by zeros.
+#pragma once
+
+#include <type_traits>
+
+#include "attn_device.h"
+
+namespace attn {
+
+constexpr int kDqWaves = 8;              // waves per dQ workgroup (32 queries each)
+constexpr int kDqBM = 32 * kDqWaves;     // query rows per dQ workgroup
+constexpr int kDqBN = 64;                // key rows per tile
+constexpr int kDqPD = 6;                 // recompute kernel: LDS reads in flight ahead of their MFMAs
+
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(Args a) {
+  constexpr int NW = kDqWaves;
+  constexpr int BM = kDqBM, BN = kDqBN;
+  constexpr int CPR = D / 8;
+  constexpr int RB = D * 2;
+  constexpr int KT = BN * RB;                // bytes of a K tile
+  constexpr int DST = 2 * NW * 2048;         // bytes of the dS^T chunks of a tile
+  constexpr int STAGE = DST + KT;
+  constexpr int NSTAGE = 3;
+  constexpr int TD = D / 32;                 // head-dim tiles of dQ
+  constexpr int KI = BN * CPR / (64 * NW);   // direct loads per wave per K tile
+  constexpr int SI = DST / 16 / (64 * NW);   // direct loads per wave per dS^T tile
+  static_assert(TD >= 2 && KI >= 1 && SI >= 1, "head dim of 64 or 128");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  const uint32_t smem_lds = lds_addr(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_id();
+  const int h = lane >> 5;
+  const int c32 = lane & 31;
+  const int sl = lane & 15;
+  const int gg = lane >> 4;
+  const int rr = sl >> 2;
+  const int tcol = 16 * (gg & 1) + 4 * (sl & 3);
+  // grid (query head x sequence, query block): the longest causal blocks of
+  // every head start first, and one head's blocks share an XCD.
+  const int hq = blockIdx.x % a.heads_q;
+  const int z = blockIdx.x / a.heads_q;
+  const Seq s = seq_info(a, z);
+  const int mb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int q0 = mb * BM;
+  if (q0 >= s.sq) return;
+  const int hd = a.head_dim;
+  const int g = hq / a.group;
+  const int off_causal = s.sk - s.sq;
+  const int qw = q0 + 32 * w;  // first query of this wave
+
+  // Key tiles this query block sees.
+  int n_end = (s.sk + BN - 1) / BN;
+  if (CAUSAL) {
+    const int q_last = min(q0 + BM, s.sq) - 1;
+    const int k_lim = q_last + off_causal;
+    n_end = k_lim < 0 ? 0 : min(n_end, k_lim / BN + 1);
+  }
+  // Last key this wave's queries see (keys past it are in chunks that may
+  // never have been written).
+  int kw_lim = s.sk - 1;
+  if (CAUSAL) kw_lim = min(kw_lim, qw + 31 + off_causal);
+
+  f32x16 dq_acc[TD];
+#pragma unroll
+  for (int t = 0; t < TD; ++t) dq_acc[t] = f32x16{};
+
+  // ---- direct loads.  K rows: swizzled 16-byte chunks as in the other
+  // kernels.  dS^T: for each of the tile's two 32-key tiles, the block's 8
+  // query-tile chunks are contiguous in the workspace (16 KiB), copied as is.
+  auto slot_off = [&](int S, int row_stride) {
+    const int r = S / CPR;
+    const int c = (S % CPR) ^ swz<CPR>(r);
+    return 8 * c < hd ? (r * row_stride + 8 * c) * 2 : kOffOOB;
+  };
+  int kdma[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) kdma[i] = slot_off((i * NW + w) * 64 + lane, (int)a.k_r);
+  const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
+  // dS^T chunk row of this head and sequence: (hq * nkt + key slot) * nqt + query tile
+  const int64_t ds_row0 = (int64_t)hq * a.ds_nkt + ds_key_slot0(a, z);
+  const int qt0 = q0 / 32;
+  const u32x4 srdS = make_srd(a.ds, a.ds_bytes);
+
+  auto prefetch = [&](int n) {
+    const int rows = min(BN, s.sk - n * BN);
+    const uint32_t stage = smem_lds + (n % NSTAGE) * STAGE;
+    const u32x4 srdK = make_srd(kbase + (int64_t)n * BN * a.k_r, ((int64_t)(rows - 1) * a.k_r + hd) * 2);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) dma16(srdK, kdma[i], stage + DST + ((i * NW + w) * 64) * 16);
+#pragma unroll
+    for (int i = 0; i < SI; ++i) {
+      // 16-byte slot S of the tile's dS^T image: key tile S / (NW*128), then
+      // the NW contiguous query-tile chunks of that key tile.
+      const int S0 = (i * NW + w) * 64;
+      const int kt = S0 / (NW * 128);
+      const int64_t byte0 = ((ds_row0 + 2 * n + kt) * a.ds_nqt + qt0) * 2048;
+      const int within = (S0 % (NW * 128)) * 16 + lane * 16;
+      // the workspace holds every chunk this block reads; the byte offset
+      // splits into a scalar base (descriptor) and a lane offset
+      u32x4 srd = srdS;
+      const uint64_t base = ((uint64_t)srd[1] << 32 | srd[0]) + (uint64_t)byte0;
+      const int64_t left = a.ds_bytes - byte0;
+      srd[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
+      srd[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xffffu);
+      srd[2] = __builtin_amdgcn_readfirstlane(left <= 0 ? 0u : (left >= 0x7fffff00 ? 0x7fffff00u : (uint32_t)left));
+      dma16_nt(srd, within, stage + S0 * 16);
+    }
+  };
+
+  // Transpose-read offsets.  dS^T chunk: key rows 4h + rr (+8) of a 16-key
+  // step, query run starting at tcol (run tcol/8 of half (tcol/4) & 1).
+  const int ds_col = 32 * ((tcol >> 2) & 1) + 8 * (tcol >> 3);
+  const int da = (4 * h + rr) * 64 + ds_col;
+  const int db = (4 * h + rr + 8) * 64 + ds_col;
+  // K tile: key rows 4h + rr (+8), head-dim columns 32t + tcol.
+  const int ka = tile_off<CPR>(4 * h + rr, tcol);
+  const int kb = tile_off<CPR>(4 * h + rr + 8, tcol);
+
+  if (n_end > 0) prefetch(0);
+  if (n_end > 1) prefetch(1);
+  for (int n = 0; n < n_end; ++n) {
+    if (n + 1 < n_end) {
+      wait_vmcnt<KI + SI>();  // tile n landed (tile n+1 may still be in flight)
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // everyone's loads of tile n; all reads of tile n-1 retired
+    if (n + 2 < n_end) prefetch(n + 2);
+    const uint8_t* st = smem + (n % NSTAGE) * STAGE;
+    const uint8_t* sK = st + DST;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      // this wave's chunk of 32-key tile kt: unwritten if above the diagonal
+      const bool live = n * BN + 32 * kt <= kw_lim;
+      const uint8_t* chunk = st + (kt * NW + w) * 2048;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        u32x4 aop = tr_frag_b(chunk, da + 16 * s2 * 64, db + 16 * s2 * 64);
+        if (!live) aop = u32x4{0u, 0u, 0u, 0u};
+        const int ro = (32 * kt + 16 * s2) * RB;
+        u32x4 bop[TD];
+#pragma unroll
+        for (int t = 0; t < TD; ++t) bop[t] = tr_frag_b(sK, (ka ^ (64 * t)) + ro, (kb ^ (64 * t)) + ro);
+#pragma unroll
+        for (int t = 0; t < TD; ++t) dq_acc[t] = mfma32<BF16>(aop, bop[t], dq_acc[t]);
+      }
+    }
+  }
+
+  // ---- dQ * scale, converted (round to nearest even).  C layout: lane =
+  // head-dim column, rows = queries 32*w + 8*(j/4) + 4*h + j%4.
+  {
+    const int rows = min(BM, s.sq - q0);
+    const uint16_t* dqb = a.dq + s.bq * a.dq_b + (int64_t)(s.q0 + q0) * a.dq_r + (int64_t)hq * a.dq_h;
+    const rsrc_t rDQ = make_rsrc(dqb, ((int64_t)(rows - 1) * a.dq_r + hd) * 2);
+#pragma unroll
+    for (int t = 0; t < TD; ++t) {
+      const int d = 32 * t + c32;
+      const bool ok = d < hd;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int qr = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
+        buf_store_u16(rDQ, ok ? (qr * (int)a.dq_r + d) * 2 : kOffOOB, to_bits<BF16>(dq_acc[t][j] * a.scale));
+      }
+    }
+  }
+}
+
+// Slot layout of one key tile of the dQ kernel and where each softmax
+// element's three dependent stages (F, E, M) go.  Slots:
+//   [0, SB)   A: S, dP of key half 0 (alternating, head-dim step = slot/2)
+//   [SB, SC)  B: dQ += dS K of the previous tile's half 1
+//   [SC, SD)  C: S, dP of key half 1
+//   [SD, N)   D: dQ += dS K of half 0
+// The softmax of half 0 runs during B (the matrix core is then busy with
+// the previous tile's dQ, which needs no score registers), that of half 1
+// during D; element e's stages sit in slots f, f+1, f+2, so every vector
+// instruction reads a value produced one slot earlier.  Stages of half 1
+// that fall past the end of the tile run at the start of the next tile's A.
+template <int NSD, int TD>
+struct DqSchedule {
+  static constexpr int SB = 2 * NSD, SC = SB + 2 * TD, SD = SC + 2 * NSD, NSLOT = SD + 2 * TD;
+  // element e's first stage; the chain of the last element ends in the
+  // last dQ slot of the phase
+  static constexpr int spread(int e, int lo, int len) { return lo + (e * (len - 2)) / 16; }
+  static constexpr bool is_sdp(int i) { return i < SB || (i >= SC && i < SD); }
+  static constexpr bool active(int i, bool first, bool drain) {
+    return (i >= SB && i < SC) ? !first : !drain;
+  }
+  static constexpr int rank(int i, bool first, bool drain) {
+    int r = 0;
+    for (int k = 0; k < i; ++k) r += active(k, first, drain) ? 1 : 0;
+    return r;
+  }
+  static constexpr int nact(bool first, bool drain) { return rank(NSLOT, first, drain); }
+  static constexpr int kth(int k, bool first, bool drain) {
+    for (int i = 0; i < NSLOT; ++i)
+      if (active(i, first, drain) && rank(i, first, drain) == k) return i;
+    return -1;
+  }
+  static constexpr int fslot_h0(int e) { return spread(e, SB, 2 * TD); }
+  static constexpr int fslot_h1(int e) { return spread(e, SD, 2 * TD); }
+  static_assert(fslot_h0(15) + 2 < SC, "half 0 must be packed within B");
+  static_assert(fslot_h1(15) + 2 < NSLOT, "half 1 must be packed within D");
+};
+
+// ---------------------------------------------------------------------------
+// dQ without the dS^T workspace (the path taken when the caller's workspace
+// holds only Delta): the kernel recomputes S^T = K Q^T and dP^T = V dO^T per
+// key tile and forms dS^T itself.  Same grid and query ownership as the
+// kernel above; each wave works every 64-key tile alone as two 32-key halves.
+// The transposed score tile puts one query per lane, so LSE and Delta are
+// per-lane constants, and dS^T leaves the MFMA in the A-operand layout of
+// dQ = dS K.
+//
+// Schedule.  The matrix-core work of one tile is a stream of slots
+//   A: S, dP of half 0      B: dQ of the previous tile's half 1
+//   C: S, dP of half 1      D: dQ of half 0
+// and the softmax of each half runs in the dQ slots after it, with one slot
+// between dependent vector instructions, so that the vector work of one
+// wave overlaps its own matrix-core work.  The K tile of the previous key
+// tile is still read in B, hence three LDS stages (3 x 32 KiB at D = 128),
+// filled by direct global->LDS loads one tile ahead.
+// ---------------------------------------------------------------------------
+template <bool BF16, int D, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_recompute_kernel(Args a) {
+  constexpr int NW = 8;
+  constexpr int BM = kDqBM, BN = kDqBN;
+  constexpr int CPR = D / 8;
+  constexpr int RB = D * 2;
+  constexpr int KT = BN * RB;                // bytes of a K (or V) tile
+  constexpr int STAGE = 2 * KT;
+  constexpr int NSTAGE = 3;
+  constexpr int TD = D / 32;                 // head-dim tiles of dQ
+  constexpr int NSD = D / 16;                // k-steps of S^T / dP^T
+  constexpr int KI = BN * CPR / (64 * NW);   // direct loads per wave per K (or V) tile
+  static_assert(TD >= 2 && KI >= 1, "head dim of 64 or 128");
+  static_assert(BM == 32 * NW && BN == 64, "32 queries per wave, two 32-key halves");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  const uint32_t smem_lds = lds_addr(smem);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = wave_id();
+  const int h = lane >> 5;
+  const int c32 = lane & 31;
+  const int sl = lane & 15;
+  const int gg = lane >> 4;
+  const int rr = sl >> 2;
+  const int tcol = 16 * (gg & 1) + 4 * (sl & 3);
+  // grid (query head x sequence, query block), as in the dK/dV kernel.
+  const int hq = blockIdx.x % a.heads_q;
+  const int z = blockIdx.x / a.heads_q;
+  const Seq s = seq_info(a, z);
+  // Causal blocks near the end of a sequence see the most keys: run them first.
+  const int mb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int q0 = mb * BM;
+  if (q0 >= s.sq) return;
+  const int hd = a.head_dim;
+  const int g = hq / a.group;
+  const int off_causal = s.sk - s.sq;
+  const int qw = q0 + 32 * w;         // first query of this wave
+  const int qi = qw + c32;            // this lane's query (a column of S^T)
+
+  // ---- Q and dO of this lane's query as B operands (k = head dim); LSE and
+  // Delta of that query.  Rows past the end read as 0.
+  u32x4 qf[NSD], df[NSD];
+  float L2, Dl;
+  {
+    const int rows = min(BM, s.sq - q0);
+    const uint16_t* qb = a.q + s.bq * a.q_b + (int64_t)(s.q0 + q0) * a.q_r + (int64_t)hq * a.q_h;
+    const uint16_t* db = a.dout + s.bq * a.do_b + (int64_t)(s.q0 + q0) * a.do_r + (int64_t)hq * a.do_h;
+    const rsrc_t rQ = make_rsrc(qb, ((int64_t)(rows - 1) * a.q_r + hd) * 2);
+    const rsrc_t rO = make_rsrc(db, ((int64_t)(rows - 1) * a.do_r + hd) * 2);
+    const int row = 32 * w + c32;
+#pragma unroll
+    for (int sd = 0; sd < NSD; ++sd) {
+      const int d0 = 16 * sd + 8 * h;
+      const bool ok = d0 < hd;
+      qf[sd] = buf_load128(rQ, ok ? (row * (int)a.q_r + d0) * 2 : kOffOOB);
+      df[sd] = buf_load128(rO, ok ? (row * (int)a.do_r + d0) * 2 : kOffOOB);
+    }
+    const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h + q0;
+    L2 = buf_load_f32(make_rsrc(a.lse_in + st0, (int64_t)rows * 4), row * 4) * kLog2e;
+    Dl = buf_load_f32(make_rsrc(a.delta + st0, (int64_t)rows * 4), row * 4);
+  }
+
+  f32x16 dq_acc[TD];
+#pragma unroll
+  for (int t = 0; t < TD; ++t) dq_acc[t] = f32x16{};
+
+  // Per-lane LDS offsets, as XOR bases (the swizzle only permutes the chunk
+  // bits, so the offset of head-dim step sd is base ^ 32*sd, of dQ tile t
+  // base ^ 64*t).  S^T/dP^T A operand: key row c32 of a half, columns
+  // 16*sd + 8*h.  dQ B operand (K, transpose read): key rows 4*h + rr (+8)
+  // of a 16-key step, columns 32*t + tcol.
+  const int svb = tile_off<CPR>(c32, 8 * h);
+  const int tab = tile_off<CPR>(4 * h + rr, tcol);
+  const int tbb = tile_off<CPR>(4 * h + rr + 8, tcol);
+
+  auto slot_off = [&](int S, int row_stride) {
+    const int r = S / CPR;
+    const int c = (S % CPR) ^ swz<CPR>(r);
+    return 8 * c < hd ? (r * row_stride + 8 * c) * 2 : kOffOOB;
+  };
+  int kdma[KI], vdma[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int S = (i * NW + w) * 64 + lane;
+    kdma[i] = slot_off(S, (int)a.k_r);
+    vdma[i] = slot_off(S, (int)a.v_r);
+  }
+
+  // Key tiles this query block sees.
+  int n_end = (s.sk + BN - 1) / BN;
+  if (CAUSAL) {
+    const int q_last = min(q0 + BM, s.sq) - 1;
+    const int k_lim = q_last + off_causal;
+    n_end = k_lim < 0 ? 0 : min(n_end, k_lim / BN + 1);
+  }
+  const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
+  const uint16_t* vbase = a.v + s.bk * a.v_b + (int64_t)s.k0 * a.v_r + (int64_t)g * a.v_h;
+
+  auto prefetch = [&](int n) {
+    const int rows = min(BN, s.sk - n * BN);
+    const uint32_t stage = smem_lds + (n % NSTAGE) * STAGE;
+    const u32x4 srdK = make_srd(kbase + (int64_t)n * BN * a.k_r, ((int64_t)(rows - 1) * a.k_r + hd) * 2);
+    const u32x4 srdV = make_srd(vbase + (int64_t)n * BN * a.v_r, ((int64_t)(rows - 1) * a.v_r + hd) * 2);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int S0 = (i * NW + w) * 64;
+      dma16(srdK, kdma[i], stage + S0 * 16);
+      dma16(srdV, vdma[i], stage + KT + S0 * 16);
+    }
+  };
+  auto tile_masked = [&](int n) {
+    return (CAUSAL && (n * BN + BN - 1 > qw + off_causal)) || (n * BN + BN > s.sk);
+  };
+
+  // Last key this lane's query sees, minus the lane's row offset 4*h in the
+  // C layout (keys past the end or above the diagonal are masked).
+  int kv_lim = s.sk - 1;
+  if (CAUSAL) kv_lim = min(kv_lim, qi + off_causal);
+  kv_lim -= 4 * h;
+
+  // Softmax state: sc/pc = current tile's S^T and (dP^T - Delta) per half;
+  // the previous tile's half 1 lives in sp/pp until its dS is packed.
+  f32x16 sc0, pc0, sc1, pc1, sp, pp;
+  u32x4 ds0[2], ds1[2], dsp[2];
+  int n_prev = 0;  // key tile whose half 1 is still pending
+
+  // Elementwise stages on element j of a score/grad pair of key half kh of
+  // key tile m.  F: scaled score (masked to -inf), E: exp2, M: dS, packed.
+  auto stageF = [&](f32x16& sv, auto jc, int m, int kh, auto mask) {
+    constexpr int j = decltype(jc)::value;
+    float t = __builtin_fmaf(sv[j], a.scale_log2, -L2);
+    if constexpr (decltype(mask)::value) {
+      // key m*BN + 32*kh + 8*(j/4) + 4*h + j%4: the wave-uniform part
+      // against this lane's limit
+      const int ks = m * BN + 32 * kh + 8 * (j >> 2) + (j & 3);
+      t = ks <= kv_lim ? t : -__builtin_inff();
+    }
+    sv[j] = t;
+  };
+  auto stageE = [&](f32x16& sv, auto jc) {
+    constexpr int j = decltype(jc)::value;
+    sv[j] = fast_exp2(sv[j]);
+  };
+  auto stageM = [&](f32x16& sv, f32x16& pv, u32x4* dsv, auto jc) {
+    constexpr int j = decltype(jc)::value;
+    pv[j] = sv[j] * (pv[j] - Dl);
+    // dS as the A operand of dQ = dS K (row = query, k = key): k-slot e of
+    // 16-key step s2 is key 16*s2 + 8*(e/4) + 4*h + e%4 of the half.
+    if constexpr (j & 1) dsv[j >> 3][(j & 7) >> 1] = pack2<BF16>(pv[j - 1], pv[j]);
+  };
+
+  using Sch = DqSchedule<NSD, TD>;
+  // One tile: FIRST = no previous tile; DRAIN = only finish the previous
+  // tile's half 1 (this wave sees no more keys).
+  auto run = [&](int n, auto first_t, auto drain_t, auto mask) {
+    constexpr bool FIRST = decltype(first_t)::value;
+    constexpr bool DRAIN = decltype(drain_t)::value;
+    constexpr int NACT = Sch::nact(FIRST, DRAIN);
+    constexpr int PD = kDqPD;  // LDS operand reads in flight ahead of their MFMA
+    // loop-variant bases so the per-step XORs are not hoisted out of the loop
+    const int svn = svb + (n % NSTAGE) * STAGE;
+    const int tan = tab + (n % NSTAGE) * STAGE, tbn = tbb + (n % NSTAGE) * STAGE;
+    const int tap = tab + (n_prev % NSTAGE) * STAGE, tbp = tbb + (n_prev % NSTAGE) * STAGE;
+    if constexpr (!DRAIN) {
+      sc0 = f32x16{};
+      pc0 = f32x16{};
+    }
+    u32x4 buf[PD];
+    auto rd = [&](auto kc) {  // LDS operand of the k-th active slot
+      constexpr int k = decltype(kc)::value;
+      constexpr int i = Sch::kth(k, FIRST, DRAIN);
+      if constexpr (Sch::is_sdp(i)) {
+        constexpr int kh = i < Sch::SB ? 0 : 1, kq = i < Sch::SB ? i : i - Sch::SC, sd = kq / 2;
+        buf[k % PD] = lds_rd128(smem, (svn ^ (32 * sd)) + kh * 32 * RB + ((kq & 1) ? KT : 0));
+      } else {
+        constexpr bool prev = i < Sch::SC;
+        constexpr int kq = prev ? i - Sch::SB : i - Sch::SD, s2 = kq / TD, t = kq % TD;
+        constexpr int ro = (32 * (prev ? 1 : 0) + 16 * s2) * RB;
+        if constexpr (prev) {
+          buf[k % PD] = tr_frag_b(smem, (tap ^ (64 * t)) + ro, (tbp ^ (64 * t)) + ro);
+        } else {
+          buf[k % PD] = tr_frag_b(smem, (tan ^ (64 * t)) + ro, (tbn ^ (64 * t)) + ro);
+        }
+      }
+    };
+    sched_fence();
+    static_for<0, (PD < NACT ? PD : NACT)>(rd);
+    sched_fence();
+    static_for<0, Sch::NSLOT>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i == Sch::SC && !DRAIN) {  // half 1 accumulators start here
+        sc1 = f32x16{};
+        pc1 = f32x16{};
+      }
+      if constexpr (Sch::active(i, FIRST, DRAIN)) {
+        constexpr int k = Sch::rank(i, FIRST, DRAIN);
+        const u32x4 op = buf[k % PD];
+        if constexpr (k + PD < NACT) rd(std::integral_constant<int, k + PD>{});
+        if constexpr (Sch::is_sdp(i)) {
+          constexpr int kq = i < Sch::SB ? i : i - Sch::SC, sd = kq / 2;
+          if constexpr (i < Sch::SB) {
+            if constexpr (kq & 1) pc0 = mfma32<BF16>(op, df[sd], pc0);
+            else sc0 = mfma32<BF16>(op, qf[sd], sc0);
+          } else {
+            if constexpr (kq & 1) pc1 = mfma32<BF16>(op, df[sd], pc1);
+            else sc1 = mfma32<BF16>(op, qf[sd], sc1);
+          }
+        } else if constexpr (i < Sch::SC) {
+          constexpr int kq = i - Sch::SB, s2 = kq / TD, t = kq % TD;
+          dq_acc[t] = mfma32<BF16>(dsp[s2], op, dq_acc[t]);
+        } else {
+          constexpr int kq = i - Sch::SD, s2 = kq / TD, t = kq % TD;
+          dq_acc[t] = mfma32<BF16>(ds0[s2], op, dq_acc[t]);
+        }
+      }
+      // softmax stages placed after this slot's matrix-core instruction
+      static_for<0, 16>([&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        constexpr int f0 = Sch::fslot_h0(e), f1 = Sch::fslot_h1(e);
+        if constexpr (!DRAIN) {  // half 0 of this tile
+          if constexpr (i == f0) stageF(sc0, ec, n, 0, mask);
+          if constexpr (i == f0 + 1) stageE(sc0, ec);
+          if constexpr (i == f0 + 2) stageM(sc0, pc0, ds0, ec);
+          // half 1 of this tile
+          if constexpr (i == f1) stageF(sc1, ec, n, 1, mask);
+          if constexpr (i == f1 + 1) stageE(sc1, ec);
+          if constexpr (i == f1 + 2) stageM(sc1, pc1, ds1, ec);
+        }
+        if constexpr (!FIRST) {  // stages of the previous tile's half 1 that spilled over
+          if constexpr (i == f1 - Sch::NSLOT) stageF(sp, ec, n_prev, 1, mask);
+          if constexpr (i == f1 + 1 - Sch::NSLOT) stageE(sp, ec);
+          if constexpr (i == f1 + 2 - Sch::NSLOT) stageM(sp, pp, dsp, ec);
+        }
+      });
+      sched_fence();
+    });
+    if constexpr (!DRAIN) {
+      sp = sc1;
+      pp = pc1;
+      dsp[0] = ds1[0];
+      dsp[1] = ds1[1];
+      n_prev = n;
+    }
+  };
+
+  // Tile loop.  The first tile is peeled (no previous half 1), the tiles
+  // that need no mask run in one loop and the masked ones (the diagonal, the
+  // ragged last tile) in a second, so the matrix-core accumulators flow
+  // through straight loops rather than branches.  A wave keeps running
+  // masked tiles past its own last visible key (they add exact zeros) until
+  // the block's last tile, so every wave takes the same barriers.
+  if (n_end > 0) {
+    prefetch(0);
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (1 < n_end) prefetch(1);
+    if (tile_masked(0)) {
+      run(0, std::true_type{}, std::false_type{}, std::true_type{});
+    } else {
+      run(0, std::true_type{}, std::false_type{}, std::false_type{});
+    }
+    int n_um = n_end;  // first tile of this wave that needs the mask
+    if (CAUSAL) {
+      const int lo = qw + off_causal - (BN - 1);  // tiles n with n*BN + BN-1 <= qw + off need none
+      n_um = lo < 0 ? 0 : min(n_um, lo / BN + 1);
+    }
+    n_um = min(n_um, s.sk / BN);
+    n_um = max(n_um, 1);
+    int n = 1;
+    for (; n < n_um; ++n) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (n + 1 < n_end) prefetch(n + 1);
+      run(n, std::false_type{}, std::false_type{}, std::false_type{});
+    }
+    for (; n < n_end; ++n) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (n + 1 < n_end) prefetch(n + 1);
+      run(n, std::false_type{}, std::false_type{}, std::true_type{});
+    }
+    run(n_end, std::false_type{}, std::true_type{}, std::false_type{});
+  }
+
+  // ---- dQ * scale, converted (round to nearest even).  C layout: lane =
+  // head-dim column, rows = queries 32*w + 8*(j/4) + 4*h + j%4.
+  {
+    const int rows = min(BM, s.sq - q0);
+    const uint16_t* dqb = a.dq + s.bq * a.dq_b + (int64_t)(s.q0 + q0) * a.dq_r + (int64_t)hq * a.dq_h;
+    const rsrc_t rDQ = make_rsrc(dqb, ((int64_t)(rows - 1) * a.dq_r + hd) * 2);
+#pragma unroll
+    for (int t = 0; t < TD; ++t) {
+      const int d = 32 * t + c32;
+      const bool ok = d < hd;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int qr = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
+        buf_store_u16(rDQ, ok ? (qr * (int)a.dq_r + d) * 2 : kOffOOB, to_bits<BF16>(dq_acc[t][j] * a.scale));
+      }
+    }
+  }
+}
+
+
+}  // namespace attn

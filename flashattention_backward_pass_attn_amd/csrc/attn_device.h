@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace attn {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -62,7 +64,22 @@ struct Args {
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   int32_t varlen;
+  // dS^T workspace written by the dK/dV kernel and read by the dQ kernel:
+  // 2 KiB chunks of 32 keys x 32 queries, chunk (head, key tile, query tile)
+  // at ((head * ds_nkt + key tile) * ds_nqt + query tile) * 2048 bytes.
+  uint16_t* ds;
+  int64_t ds_bytes;   // size of that region
+  int64_t ds_nkt;     // key-tile slots per head
+  int32_t ds_nqt;     // query-tile slots per key tile
 };
+
+// Slot of the first 32-key tile of sequence z in the dS^T workspace.  Each
+// sequence gets 4 slots per started 128-key block (its dK/dV workgroups
+// write whole blocks), so consecutive sequences never overlap.
+__device__ inline int64_t ds_key_slot0(const Args& a, int z) {
+  const int64_t kr0 = a.varlen ? (int64_t)a.cu_k[z] : (int64_t)z * a.seqlen_k;
+  return 4 * (kr0 / 128) + 4 * (int64_t)z;
+}
 
 // Per-(sequence) geometry: row offsets into packed tensors and lengths.
 struct Seq {
@@ -245,6 +262,11 @@ __device__ __forceinline__ void buf_store_u16(rsrc_t r, int off, uint16_t v) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
 
+// 16-byte store, non-temporal (written once, read once much later).
+__device__ __forceinline__ void buf_store128_nt(rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2 /* nt */);
+}
+
 __device__ __forceinline__ void buf_store_f32(rsrc_t r, int off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
 }
@@ -278,6 +300,12 @@ __device__ __forceinline__ u32x4 make_srd(const void* base, int64_t num_bytes) {
 
 __device__ __forceinline__ void dma16(u32x4 srd, int off, uint32_t lds_byte) {
   __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte) : "memory");
+}
+
+// The same, marked non-temporal (data read once: keep it out of the caches'
+// reuse sets).
+__device__ __forceinline__ void dma16_nt(u32x4 srd, int off, uint32_t lds_byte) {
+  __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte) : "memory");
 }
 
 __device__ __forceinline__ void dma4(u32x4 srd, int off, uint32_t lds_byte) {
@@ -340,6 +368,15 @@ __device__ __forceinline__ void pipeline_hint() {
 }
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Compile-time iteration: f(integral_constant<int, B>), ..., f(<E-1>).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 
 // ---------------------------------------------------------------------------

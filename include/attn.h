@@ -93,11 +93,24 @@ attn_status attn_fwd(const attn_params *p, const void *q, const void *k, const v
                      void *o, float *lse, void *stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these parameters: Delta, fp32
- * laid out like lse (the flash-attention CK mha_bwd.cpp page's softmax_d),
- * rounded up to 256 bytes.  Never allocates.
+ * Bytes of device workspace for the fast backward path: Delta, fp32 laid out
+ * like lse (the flash-attention CK mha_bwd.cpp page's softmax_d), rounded up
+ * to 256 bytes, followed by dS = P o (dP - Delta) in the input dtype as
+ * 32 x 32 tiles (about 2 * Hq * Sq * Sk bytes, independent of `causal`;
+ * varlen: bounded by 2 * Hq * total_k * max_seqlen_q plus padding).  With it
+ * the dK/dV kernel, which forms dS anyway, stores it and the dQ kernel is a
+ * plain product dQ = scale * dS K over it.  Never allocates.
  */
 attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
+
+/*
+ * Bytes of the smallest workspace attn_bwd accepts: Delta only.  With a
+ * workspace smaller than attn_bwd_workspace_size() (but at least this), the
+ * dQ kernel recomputes S, dP and dS per key tile instead of reading them:
+ * more arithmetic, no quadratic memory.  Results are identical in value up
+ * to rounding of the same operations and equally deterministic.
+ */
+attn_status attn_bwd_workspace_size_min(const attn_params *p, size_t *bytes);
 
 /*
  * Backward: dQ, dK, dV of sum(O o dO).
@@ -109,15 +122,16 @@ attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
  *   q, k, v, o, dout, lse: inputs (o, lse from attn_fwd), read only.
  *   dq [.., Sq, H, d], dk, dv [.., Sk, Hk, d]: outputs, fully overwritten; dK
  *   and dV of a KV head are summed over the query heads of its group.
- *   workspace: device buffer of at least attn_bwd_workspace_size() bytes,
- *   256-byte aligned; its contents on entry do not matter.
+ *   workspace: device buffer, 256-byte aligned, of at least
+ *   attn_bwd_workspace_size_min() bytes; attn_bwd_workspace_size() bytes
+ *   select the faster path (see there).  Its contents on entry do not matter.
  *   delta_out: NULL, or a device fp32 buffer laid out like lse that receives
  *   Delta = rowsum(dO o O) (for tests).
  * Three launches on `stream`: the preprocess (Delta), a KV-stationary kernel
- * for dK and dV, and a Q-stationary kernel for dQ that sums the key blocks in
- * ascending order in registers.  No atomics are used, so every output is
- * bit-identical from run to run; `deterministic` is accepted and always
- * satisfied.
+ * for dK and dV (which also stores dS with the full workspace), and a
+ * Q-stationary kernel for dQ that sums the key blocks in ascending order in
+ * registers.  No atomics are used, so every output is bit-identical from run
+ * to run; `deterministic` is accepted and always satisfied.
  * Sq == 0 gives dK = dV = 0; Sk == 0 gives dQ = 0.
  * Errors: as attn_fwd, plus ATTN_ERR_WORKSPACE_TOO_SMALL.
  */
@@ -132,9 +146,10 @@ attn_status attn_bwd(const attn_params *p, const void *q, const void *k, const v
  * (bitwise OR of ATTN_PHASE_*): the preprocess, then dK/dV, then dQ.
  * attn_bwd == attn_bwd_phases(..., ATTN_PHASE_ALL).  Lets a caller time or
  * schedule the kernels separately.  The dK/dV and dQ kernels read Delta from
- * `workspace`, which the preprocess writes; they do not depend on each other.
- * Running a gradient phase without a preprocess on the same workspace gives
- * unspecified (but in-bounds) results.  Arguments, validation and errors as
+ * `workspace`, which the preprocess writes; with the full workspace the dQ
+ * kernel also reads the dS the dK/dV kernel stored there, so the phases must
+ * run in this order on one workspace.  A gradient phase whose inputs were not
+ * produced that way gives unspecified (but in-bounds) results.  Arguments, validation and errors as
  * attn_bwd; phases == 0 or an unknown bit is ATTN_ERR_INVALID_ARGUMENT.
  */
 #define ATTN_PHASE_PREPROCESS 1u

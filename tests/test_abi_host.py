@@ -117,11 +117,16 @@ def test_half_varlen_rejected(clib):
 def test_workspace_size_and_too_small(clib):
     p = _params()
     n = ctypes.c_size_t(0)
+    nmin = ctypes.c_size_t(0)
     assert clib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == fa.ATTN_OK
+    assert clib.attn_bwd_workspace_size_min(ctypes.byref(p), ctypes.byref(nmin)) == fa.ATTN_OK
     stat = 2 * 8 * 128  # Delta: fp32 [B, H, Sq]
-    assert n.value >= stat * 4 and n.value % 256 == 0
-    assert _bwd(clib, p, ws_bytes=n.value - 1) == fa.ATTN_ERR_WORKSPACE_TOO_SMALL
-    # the workspace does not depend on the deterministic flag (no dQ accumulator)
+    assert nmin.value >= stat * 4 and nmin.value % 256 == 0
+    # the full workspace adds the dS tiles: at least Hq * Sq * Sk bf16/fp16 values per sequence
+    assert n.value >= nmin.value + 2 * 8 * 128 * 128 * 2 and n.value % 256 == 0
+    # below the minimum nothing is launched
+    assert _bwd(clib, p, ws_bytes=nmin.value - 1) == fa.ATTN_ERR_WORKSPACE_TOO_SMALL
+    # neither size depends on the deterministic flag (no dQ accumulator)
     pd = _params(deterministic=1)
     nd = ctypes.c_size_t(0)
     assert clib.attn_bwd_workspace_size(ctypes.byref(pd), ctypes.byref(nd)) == fa.ATTN_OK

@@ -65,6 +65,30 @@ def test_small_parity(lib, case):
     _compare(out, ref, case[1])
 
 
+@pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_small_parity_minimal_workspace(lib, case):
+    """The path for a Delta-only workspace: the dQ kernel recomputes dS."""
+    print(f"[gpu] small parity, minimal workspace {case[0]}", flush=True)
+    inp = _inputs(case, seed=4321)
+    causal = case[8]
+    out = gpu_run(lib, inp, causal, minimal_workspace=True)
+    ref = oracle_run(inp, causal)
+    _compare(out, ref, case[1])
+
+
+def test_both_workspace_paths_agree(lib):
+    """dK, dV identical; dQ within the rounding of the same operations."""
+    print("[gpu] fast vs minimal workspace, ragged causal bf16 d128", flush=True)
+    case = SMALL_CASES[1]
+    inp = _inputs(case, seed=7)
+    a = gpu_run(lib, inp, True)
+    b = gpu_run(lib, inp, True, minimal_workspace=True)
+    for n in ("dk", "dv"):
+        assert np.array_equal(_bits(a[n]), _bits(b[n])), n
+    da, db = to_f64(a["dq"]), to_f64(b["dq"])
+    assert np.max(np.abs(da - db)) <= 1e-2 * np.max(np.abs(db))
+
+
 @pytest.mark.parametrize("case", [SMALL_CASES[1], SMALL_CASES[4], SMALL_CASES[6]], ids=lambda c: c[0])
 def test_small_parity_deterministic(lib, case):
     print(f"[gpu] deterministic parity {case[0]}", flush=True)
