@@ -38,12 +38,14 @@ import workloads  # noqa: E402
 MFMA_PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_backward_pass_attn_amd/csrc/attn_bwd_split.h",
+                  "flashattention_backward_pass_attn_amd/csrc/attn_bwd_dq.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_device.h"]
 TRAFFIC_FILE = "profiles/bwd_{kernel}_traffic_{workload}.json"
 # Matrix-core work of each gradient kernel, in units of 2*b*h*Sq*Sk*d (halved
-# when causal): dK/dV does S, dP, dV, dK; dQ does S, dP, dQ.  The metric counts
-# the method's 5 contractions (10*b*h*Sq*Sk*d) for the whole backward.
-KERNEL_UNITS = {"attn_bwd_dkdv_kernel": 4, "attn_bwd_dq_kernel": 3}
+# when causal): dK/dV does S, dP, dV, dK; dQ (over the stored dS, the path the
+# default workspace selects) does dQ only.  The metric counts the method's 5
+# contractions (10*b*h*Sq*Sk*d) for the whole backward.
+KERNEL_UNITS = {"attn_bwd_dkdv_kernel": 4, "attn_bwd_dq_kernel": 1}
 
 
 def log(*a):
@@ -276,6 +278,19 @@ def main(argv=None):
         kfl = flops / 5.0 * KERNEL_UNITS[name]
         per_kernel[name] = {"ms": round(ms, 4), "tflops": round(kfl / (ms * 1e-3) / 1e12, 2),
                             "frac": round(kfl / (ms * 1e-3) / 1e12 / peak, 4), "flop": kfl}
+    # the dQ kernel streams the stored dS (2 bytes per visible (query, key)
+    # pair = 2 * flops / (10 * d)) plus K and dQ once: HBM-bound
+    elem = 2
+    k_bytes = elem * w.head_dim * (int(inp["lengths_k"].sum()) * w.heads_kv if w.varlen
+                                   else w.batch * w.seqlen * w.heads_kv)
+    q_bytes = elem * w.head_dim * (int(inp["lengths_q"].sum()) * w.heads_q if w.varlen
+                                   else w.batch * w.seqlen * w.heads_q)
+    dq_bytes = elem * flops / (10.0 * w.head_dim) + k_bytes + q_bytes
+    per_kernel["attn_bwd_dq_kernel"].update({
+        "bound": "hbm", "bytes": dq_bytes,
+        "gbs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(dq_bytes / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    per_kernel["attn_bwd_dkdv_kernel"]["bound"] = "mfma"
     dom = max(kernels, key=kernels.get)
     traffic = load_traffic(w.name, dom.replace("attn_bwd_", "").replace("_kernel", ""))
     roofline = {
