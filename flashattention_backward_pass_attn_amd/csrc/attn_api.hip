@@ -221,7 +221,7 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   a.out_o = static_cast<uint16_t*>(o);
   a.lse_out = lse;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  dim3 grid((p->seqlen_q + attn::kFwdBM - 1) / attn::kFwdBM, p->heads_q, p->batch);
+  dim3 grid(p->heads_q * p->batch, (p->seqlen_q + attn::kFwdBM - 1) / attn::kFwdBM, 1);
   const int dt = dtile_for(p->head_dim);
   if (p->dtype == ATTN_BF16) launch_fwd<true>(a, dt, p->causal, grid, hs);
   else launch_fwd<false>(a, dt, p->causal, grid, hs);

@@ -27,7 +27,7 @@ constexpr int kFwdBM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kFwdBN = 64;   // key rows per iteration
 
 template <bool BF16, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(Args a) {
   constexpr int BM = kFwdBM, BN = kFwdBN, LD = D + 8;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int NCH = BN * CPR / 256;     // chunks per thread per K (or V) block
@@ -43,10 +43,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(Args a) {
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int c32 = lane & 31;
-  const int hq = blockIdx.y;
-  const int z = blockIdx.z;
+  // grid (query head x sequence, query block), block index slowest: the
+  // longest causal blocks of every head start first, and one head's blocks
+  // share an XCD (and its L2 copy of K and V).
+  const int hq = blockIdx.x % a.heads_q;
+  const int z = blockIdx.x / a.heads_q;
   const Seq s = seq_info(a, z);
-  const int qb0 = blockIdx.x * BM;
+  const int qb0 = (CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y) * BM;
   if (qb0 >= s.sq) return;
   const int g = hq / a.group;
   const int hd = a.head_dim;
