@@ -37,9 +37,9 @@ constexpr int kDkvBN = 128;   // key rows per dK/dV workgroup
 //   wave w: key rows 32*(w&3) .. +32 of the block; query half (w>>2) of each
 //   64-query tile for S = Q K^T and dP = dO V^T; head-dim half (w>>2) for
 //   dV += P^T dO and dK += dS^T Q.
-// LDS (D = 128): two stages of {Q, dO, LSE, Delta} (2 x 32.5 KiB, swizzled,
-// filled by direct global->LDS loads one tile ahead) + the P/dS exchange
-// (8 x 4 KiB).
+// LDS (D = 128): three stages of {Q, dO, LSE, Delta} (3 x 32.5 KiB,
+// swizzled, filled by direct global->LDS loads two tiles ahead) + the P/dS
+// exchange (8 x 4 KiB).
 // ---------------------------------------------------------------------------
 template <bool BF16, int D, bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -52,10 +52,13 @@ void attn_bwd_dkdv_kernel(Args a) {
   constexpr int TD = D / 32;                 // head-dim tiles
   constexpr int TDH = TD / 2;                // head-dim tiles per half
   constexpr int QI = BM * CPR / 512;         // direct loads per wave per Q (or dO) tile
+  constexpr int NPF = 2 * QI + 1;            // direct loads per wave per tile (Q, dO, one stat row)
+  constexpr int NSTAGE = 3;
   constexpr int XB = 4 * 16 * 64;            // exchange bytes per wave
+  constexpr int SINK = NSTAGE * STAGE + 8 * XB;  // 256 bytes the idle waves' stat loads land in
   static_assert(TDH >= 1 && QI >= 1, "head dim of 64 or 128");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + 8 * XB];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SINK + 256];
   const uint32_t smem_lds = lds_addr(smem);
 
   const int tid = threadIdx.x;
@@ -108,9 +111,9 @@ void attn_bwd_dkdv_kernel(Args a) {
   }
 
   // ---- Per-lane LDS byte offsets (swizzle folded in; rows modulo 16).
-  int sv[D / 16];  // S/dP A operand: row 32*half + c32, columns 16*sd + 8*h
-#pragma unroll
-  for (int sd = 0; sd < D / 16; ++sd) sv[sd] = 32 * half * RB + tile_off<CPR>(c32, 16 * sd + 8 * h);
+  // S/dP A operand: row 32*half + c32, columns 16*sd + 8*h.  The swizzle
+  // only permutes the chunk bits, so step sd is at svb ^ 32*sd.
+  const int svb = 32 * half * RB + tile_off<CPR>(c32, 8 * h);
   int ta[TDH], tb[TDH];  // dV/dK B operand: rows 4*h + rr (+8), columns of this wave's head-dim tiles
 #pragma unroll
   for (int t = 0; t < TDH; ++t) {
@@ -118,8 +121,8 @@ void attn_bwd_dkdv_kernel(Args a) {
     ta[t] = tile_off<CPR>(4 * h + rr, col);
     tb[t] = tile_off<CPR>(4 * h + rr + 8, col);
   }
-  uint8_t* const xown = smem + 2 * STAGE + w * XB + lane * 16;
-  const uint8_t* const xpar = smem + 2 * STAGE + (w ^ 4) * XB + lane * 16;
+  uint8_t* const xown = smem + NSTAGE * STAGE + w * XB + lane * 16;
+  const uint8_t* const xpar = smem + NSTAGE * STAGE + (w ^ 4) * XB + lane * 16;
 
   auto slot_off = [&](int S, int row_stride) {
     const int r = S / CPR;
@@ -146,42 +149,58 @@ void attn_bwd_dkdv_kernel(Args a) {
     const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h;
     // this wave's row of dS^T chunks for query head hq (query tile qt at + qt * 2 KiB)
     const uint8_t* ds_head = reinterpret_cast<const uint8_t*>(a.ds) +
-                             __builtin_amdgcn_readfirstlane((int)0) +
                              ((int64_t)hq * a.ds_nkt + ds_slot) * (int64_t)a.ds_nqt * 2048;
 
     // Tile m into stage `st`: Q, dO, LSE, Delta.  Rows past the end read as 0;
-    // their P and dS then contribute nothing (Q = dO = 0).
-    auto prefetch = [&](int m, int st) {
-      const int rows = min(BM, s.sq - m * BM);
+    // their P and dS then contribute nothing (Q = dO = 0).  Every wave issues
+    // exactly NPF loads per call, so the memory-counter waits below are
+    // exact: for real == false (no such tile) the loads have an empty range,
+    // land zeros in a stage nobody reads again, and the idle waves' stat
+    // loads land in the sink.
+    auto prefetch = [&](int m, int st, bool real) {
+      const int rows = real ? min(BM, s.sq - m * BM) : 0;
       const uint32_t stage = smem_lds + st * STAGE;
-      const u32x4 srdQ = make_srd(qb + (int64_t)m * BM * a.q_r, ((int64_t)(rows - 1) * a.q_r + hd) * 2);
-      const u32x4 srdO = make_srd(db + (int64_t)m * BM * a.do_r, ((int64_t)(rows - 1) * a.do_r + hd) * 2);
+      const int64_t nq = rows > 0 ? ((int64_t)(rows - 1) * a.q_r + hd) * 2 : 0;
+      const int64_t no = rows > 0 ? ((int64_t)(rows - 1) * a.do_r + hd) * 2 : 0;
+      const u32x4 srdQ = make_srd(qb + (int64_t)m * BM * a.q_r, nq);
+      const u32x4 srdO = make_srd(db + (int64_t)m * BM * a.do_r, no);
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
         const int S0 = (i * 8 + w) * 64;
         dma16(srdQ, qdma[i], stage + S0 * 16);
         dma16(srdO, dodma[i], stage + TILE + S0 * 16);
       }
-      if (w == 0) {
-        dma4(make_srd(a.lse_in + st0 + m * BM, (int64_t)rows * 4), lane * 4, stage + 2 * TILE);
-      } else if (w == 1) {
-        dma4(make_srd(a.delta + st0 + m * BM, (int64_t)rows * 4), lane * 4, stage + 2 * TILE + BM * 4);
-      }
+      const float* srow = w == 0 ? a.lse_in : a.delta;
+      const int64_t nstat = w < 2 ? (int64_t)rows * 4 : 0;
+      const uint32_t sdst = w < 2 ? stage + 2 * TILE + w * BM * 4 : smem_lds + SINK;
+      dma4(make_srd(srow + st0 + m * BM, nstat), lane * 4, sdst);
     };
 
     // Before refilling stage 0 for a new head, every wave must be done with
     // the previous head's last tile.
     if (hq != g * a.group) lds_barrier();
-    prefetch(m_begin, 0);
-    wait_vmcnt<0>();
+    prefetch(m_begin, 0, true);
+    prefetch(m_begin + 1, 1, m_begin + 1 < m_end);
+    {
+      // two empty stores stand in for the previous tile's dS^T stores, so
+      // the wait at the end of every tile counts the same operations
+      const rsrc_t none = make_rsrc(a.q, 0);
+      buf_store128_nt(none, 0, u32x4{0u, 0u, 0u, 0u});
+      buf_store128_nt(none, 16, u32x4{0u, 0u, 0u, 0u});
+    }
+    wait_vmcnt<NPF + 2>();  // tile m_begin landed
     lds_barrier();
+    int st = 0;
     for (int m = m_begin; m < m_end; ++m) {
-      const int st = (m - m_begin) & 1;
-      // the other stage was last read in the previous tile, which every wave
-      // has finished (barrier at the end of the loop body)
-      if (m + 1 < m_end) prefetch(m + 1, st ^ 1);
+      // stage (st + 2) % 3 was last read in the previous tile, which every
+      // wave has finished (barrier at the end of the loop body)
+      const int st2 = st == 0 ? 2 : st - 1;
+      prefetch(m + 2, st2, m + 2 < m_end);
 
       const uint8_t* sQ = smem + st * STAGE;
+      // per-tile base (stage offsets leave the chunk bits alone), so the
+      // per-step XORs are not hoisted out of the loop into 8 registers
+      const int svn = svb + st * STAGE;
       const uint8_t* sdO = sQ + TILE;
       const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
       const float* sDl = sL + BM;
@@ -201,8 +220,8 @@ void attn_bwd_dkdv_kernel(Args a) {
         constexpr int NS = D / 16, PD = 3;
         u32x4 fq[PD], fo[PD];
         auto rd = [&](int sd, int slot) {
-          fq[slot] = lds_rd128(sQ, sv[sd]);
-          fo[slot] = lds_rd128(sdO, sv[sd]);
+          fq[slot] = lds_rd128(smem, svn ^ (32 * sd));
+          fo[slot] = lds_rd128(smem, (svn ^ (32 * sd)) + TILE);
         };
         sched_fence();
 #pragma unroll
@@ -312,10 +331,12 @@ void attn_bwd_dkdv_kernel(Args a) {
           sched_fence();
         }
       }
-      // the next tile's loads (issued at the top, before this tile's two
-      // dS^T stores, which may stay in flight: the counter retires in order)
-      wait_vmcnt<2>();
+      // Tile m+1 landed.  Issued after its loads: the previous tile's two
+      // dS^T stores, tile m+2's loads and this tile's two stores, which may
+      // all stay in flight (the counter retires in order).
+      wait_vmcnt<NPF + 4>();
       lds_barrier();  // everyone's loads; all reads of this stage retired
+      st = st == 2 ? 0 : st + 1;
     }
   }
 
