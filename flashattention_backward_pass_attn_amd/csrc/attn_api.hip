@@ -60,6 +60,17 @@ attn_status validate_common(const attn_params* p) {
   if (p->heads_q > 65535 || p->batch > 65535) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)p->heads_q * p->batch > 0x7fffffff) return ATTN_ERR_UNSUPPORTED;
   if (p->seqlen_q > 65535 * 64 || p->seqlen_k > 65535 * 64) return ATTN_ERR_UNSUPPORTED;
+  // the kernels address one head of one sequence with 32-bit byte offsets
+  // (plus a sentinel just below 2^31): each tensor's per-head extent must
+  // stay under 1 GiB
+  {
+    const attn_strides* qs[] = {&p->q, &p->o, &p->dout, &p->dq};
+    const attn_strides* ks[] = {&p->k, &p->v, &p->dk, &p->dv};
+    for (const attn_strides* st : qs)
+      if ((int64_t)p->seqlen_q * st->row * 2 >= (int64_t)1 << 30) return ATTN_ERR_UNSUPPORTED;
+    for (const attn_strides* st : ks)
+      if ((int64_t)p->seqlen_k * st->row * 2 >= (int64_t)1 << 30) return ATTN_ERR_UNSUPPORTED;
+  }
   return ATTN_OK;
 }
 
@@ -263,7 +274,9 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
     if (!aligned16(ptr)) return ATTN_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (workspace_bytes_given < workspace_bytes_min(p)) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  const bool use_ds = workspace_bytes_given >= workspace_bytes(p);
+  // the stored-dS path addresses one head's dS tiles with 32-bit offsets
+  const bool ds_fits = (int64_t)(4 * ((p->seqlen_k + 127) / 128) + 4) * ds_nqt(p) * 2048 < ((int64_t)1 << 30);
+  const bool use_ds = ds_fits && workspace_bytes_given >= workspace_bytes(p);
 
   Args a = make_args(p);
   a.q = static_cast<const uint16_t*>(q);

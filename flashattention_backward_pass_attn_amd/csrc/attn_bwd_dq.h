@@ -103,34 +103,27 @@ void attn_bwd_dq_kernel(Args a) {
 #pragma unroll
   for (int i = 0; i < KI; ++i) kdma[i] = slot_off((i * NW + w) * 64 + lane, (int)a.k_r);
   const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
-  // dS^T chunk row of this head and sequence: (hq * nkt + key slot) * nqt + query tile
-  const int64_t ds_row0 = (int64_t)hq * a.ds_nkt + ds_key_slot0(a, z);
-  const int qt0 = q0 / 32;
-  const u32x4 srdS = make_srd(a.ds, a.ds_bytes);
+  // One descriptor for the head's K rows and one for this block's dS^T
+  // chunks (from key slot 0, query tile q0/32 on); a tile is a 32-bit lane
+  // offset into them (extents below 1 GiB, checked on the host).  K rows
+  // past the end and columns past head_dim read as zero.
+  const u32x4 srdK = make_srd(kbase, ((int64_t)(s.sk - 1) * a.k_r + hd) * 2);
+  const int64_t ds_base = (((int64_t)hq * a.ds_nkt + ds_key_slot0(a, z)) * a.ds_nqt + q0 / 32) * 2048;
+  const u32x4 srdS = make_srd(reinterpret_cast<const uint8_t*>(a.ds) + ds_base, a.ds_bytes - ds_base);
 
   auto prefetch = [&](int n) {
-    const int rows = min(BN, s.sk - n * BN);
     const uint32_t stage = smem_lds + (n % NSTAGE) * STAGE;
-    const u32x4 srdK = make_srd(kbase + (int64_t)n * BN * a.k_r, ((int64_t)(rows - 1) * a.k_r + hd) * 2);
+    const uint32_t tk = (uint32_t)(n * BN) * (uint32_t)a.k_r * 2u;
 #pragma unroll
-    for (int i = 0; i < KI; ++i) dma16(srdK, kdma[i], stage + DST + ((i * NW + w) * 64) * 16);
+    for (int i = 0; i < KI; ++i) dma16(srdK, (int)((uint32_t)kdma[i] + tk), stage + DST + ((i * NW + w) * 64) * 16);
 #pragma unroll
     for (int i = 0; i < SI; ++i) {
       // 16-byte slot S of the tile's dS^T image: key tile S / (NW*128), then
       // the NW contiguous query-tile chunks of that key tile.
       const int S0 = (i * NW + w) * 64;
       const int kt = S0 / (NW * 128);
-      const int64_t byte0 = ((ds_row0 + 2 * n + kt) * a.ds_nqt + qt0) * 2048;
-      const int within = (S0 % (NW * 128)) * 16 + lane * 16;
-      // the workspace holds every chunk this block reads; the byte offset
-      // splits into a scalar base (descriptor) and a lane offset
-      u32x4 srd = srdS;
-      const uint64_t base = ((uint64_t)srd[1] << 32 | srd[0]) + (uint64_t)byte0;
-      const int64_t left = a.ds_bytes - byte0;
-      srd[0] = __builtin_amdgcn_readfirstlane((uint32_t)base);
-      srd[1] = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32) & 0xffffu);
-      srd[2] = __builtin_amdgcn_readfirstlane(left <= 0 ? 0u : (left >= 0x7fffff00 ? 0x7fffff00u : (uint32_t)left));
-      dma16_nt(srd, within, stage + S0 * 16);
+      const uint32_t off = (uint32_t)((2 * n + kt) * a.ds_nqt) * 2048u + (uint32_t)((S0 % (NW * 128)) * 16 + lane * 16);
+      dma16_nt(srdS, (int)off, stage + S0 * 16);
     }
   };
 

@@ -148,6 +148,7 @@ void attn_bwd_dkdv_kernel(Args a) {
     const uint16_t* db = a.dout + s.bq * a.do_b + (int64_t)s.q0 * a.do_r + (int64_t)hq * a.do_h;
     const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h;
     // this wave's row of dS^T chunks for query head hq (query tile qt at + qt * 2 KiB)
+    // this wave's row of dS^T chunks for query head hq (query tile qt at + qt * 2 KiB)
     const uint8_t* ds_head = reinterpret_cast<const uint8_t*>(a.ds) +
                              ((int64_t)hq * a.ds_nkt + ds_slot) * (int64_t)a.ds_nqt * 2048;
 
@@ -157,23 +158,27 @@ void attn_bwd_dkdv_kernel(Args a) {
     // exact: for real == false (no such tile) the loads have an empty range,
     // land zeros in a stage nobody reads again, and the idle waves' stat
     // loads land in the sink.
+    // One descriptor per head (the sequence's rows of Q and dO, its LSE or
+    // Delta row), built once; a tile is a 32-bit lane offset into it, so the
+    // per-tile cost is a few vector adds.  Offsets past the range read as
+    // zero: rows past the end, the columns past head_dim (offset kOffOOB)
+    // and, for real == false, the whole tile.  Head extents are below 2 GiB
+    // (checked on the host), so no offset wraps.
+    const u32x4 srdQh = make_srd(qb, ((int64_t)(s.sq - 1) * a.q_r + hd) * 2);
+    const u32x4 srdOh = make_srd(db, ((int64_t)(s.sq - 1) * a.do_r + hd) * 2);
+    const u32x4 srdSh = make_srd((w == 0 ? a.lse_in : a.delta) + st0, w < 2 ? (int64_t)s.sq * 4 : 0);
     auto prefetch = [&](int m, int st, bool real) {
-      const int rows = real ? min(BM, s.sq - m * BM) : 0;
       const uint32_t stage = smem_lds + st * STAGE;
-      const int64_t nq = rows > 0 ? ((int64_t)(rows - 1) * a.q_r + hd) * 2 : 0;
-      const int64_t no = rows > 0 ? ((int64_t)(rows - 1) * a.do_r + hd) * 2 : 0;
-      const u32x4 srdQ = make_srd(qb + (int64_t)m * BM * a.q_r, nq);
-      const u32x4 srdO = make_srd(db + (int64_t)m * BM * a.do_r, no);
+      const uint32_t tq = real ? (uint32_t)(m * BM) * (uint32_t)a.q_r * 2u : (uint32_t)kOffOOB;
+      const uint32_t to = real ? (uint32_t)(m * BM) * (uint32_t)a.do_r * 2u : (uint32_t)kOffOOB;
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
         const int S0 = (i * 8 + w) * 64;
-        dma16(srdQ, qdma[i], stage + S0 * 16);
-        dma16(srdO, dodma[i], stage + TILE + S0 * 16);
+        dma16(srdQh, (int)((uint32_t)qdma[i] + tq), stage + S0 * 16);
+        dma16(srdOh, (int)((uint32_t)dodma[i] + to), stage + TILE + S0 * 16);
       }
-      const float* srow = w == 0 ? a.lse_in : a.delta;
-      const int64_t nstat = w < 2 ? (int64_t)rows * 4 : 0;
       const uint32_t sdst = w < 2 ? stage + 2 * TILE + w * BM * 4 : smem_lds + SINK;
-      dma4(make_srd(srow + st0 + m * BM, nstat), lane * 4, sdst);
+      dma4(srdSh, (int)(real ? (uint32_t)(m * BM + lane) * 4u : (uint32_t)kOffOOB), sdst);
     };
 
     // Before refilling stage 0 for a new head, every wave must be done with

@@ -99,7 +99,9 @@ attn_status attn_fwd(const attn_params *p, const void *q, const void *k, const v
  * 32 x 32 tiles (about 2 * Hq * Sq * Sk bytes, independent of `causal`;
  * varlen: bounded by 2 * Hq * total_k * max_seqlen_q plus padding).  With it
  * the dK/dV kernel, which forms dS anyway, stores it and the dQ kernel is a
- * plain product dQ = scale * dS K over it.  Never allocates.
+ * plain product dQ = scale * dS K over it.  (When one head's dS tiles
+ * would span 1 GiB or more -- sequences of roughly 23K keys and up -- the
+ * recompute path below is used whatever the workspace.)  Never allocates.
  */
 attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
 
