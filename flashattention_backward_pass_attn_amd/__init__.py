@@ -197,7 +197,7 @@ def attn_fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = Non
 
 def bwd_workspace_size(p: attn_params, minimal: bool = False) -> int:
     """Workspace bytes of the fast path (Delta + stored dS), or with ``minimal``
-    the smallest accepted workspace (Delta only; dQ then recomputes dS)."""
+    the smallest accepted workspace (row statistics only; dQ then recomputes dS)."""
     n = ctypes.c_size_t(0)
     lib = load_library()
     fn = lib.attn_bwd_workspace_size_min if minimal else lib.attn_bwd_workspace_size

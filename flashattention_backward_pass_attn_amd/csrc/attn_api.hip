@@ -85,9 +85,12 @@ int64_t stat_count(const attn_params* p) {
                       : (int64_t)p->batch * p->heads_q * p->seqlen_q;
 }
 
-size_t delta_bytes(const attn_params* p) {
+// One fp32 row statistic laid out like lse, and the workspace's statistics
+// region: Delta, then LSE * log2(e) (both written by the preprocess).
+size_t stat_bytes(const attn_params* p) {
   return round_up((size_t)stat_count(p) * sizeof(float), kAlign);
 }
+size_t delta_bytes(const attn_params* p) { return 2 * stat_bytes(p); }
 
 // dS^T chunk grid (see Args::ds): 4 key-tile slots per 128-key block of each
 // sequence plus 4 per sequence for the ragged blocks, and query tiles in
@@ -102,9 +105,9 @@ size_t ds_bytes(const attn_params* p) {
   return round_up((size_t)p->heads_q * (size_t)ds_nkt(p) * (size_t)ds_nqt(p) * 2048u, kAlign);
 }
 
-// Full workspace: Delta then the dS^T chunks (the dQ kernel is then a plain
-// product over them).  Minimal workspace: Delta only (the dQ kernel then
-// recomputes dS).
+// Full workspace: the statistics then the dS^T chunks (the dQ kernel is then
+// a plain product over them).  Minimal workspace: the statistics only (the dQ
+// kernel then recomputes dS).
 size_t workspace_bytes(const attn_params* p) { return delta_bytes(p) + ds_bytes(p); }
 size_t workspace_bytes_min(const attn_params* p) { return delta_bytes(p); }
 
@@ -290,6 +293,7 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   a.lse_in = lse;
   a.delta_out = delta_out;
   a.delta = static_cast<float*>(workspace);
+  a.lse2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + stat_bytes(p));
   if (use_ds) {
     a.ds = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + delta_bytes(p));
     a.ds_bytes = (int64_t)ds_bytes(p);

@@ -49,6 +49,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(Args a) {
     if (sub == 0 && r < s.sq) {
       a.delta[st0 + r] = acc;
       if (a.delta_out) a.delta_out[st0 + r] = acc;
+    } else if (sub == 1 && r < s.sq) {
+      // the exp2-domain LSE the dK/dV kernel stages with Delta
+      a.lse2[st0 + r] = a.lse_in[st0 + r] * kLog2e;
     }
   }
 }

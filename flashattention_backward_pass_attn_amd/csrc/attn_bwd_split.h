@@ -166,7 +166,7 @@ void attn_bwd_dkdv_kernel(Args a) {
     // (checked on the host), so no offset wraps.
     const u32x4 srdQh = make_srd(qb, ((int64_t)(s.sq - 1) * a.q_r + hd) * 2);
     const u32x4 srdOh = make_srd(db, ((int64_t)(s.sq - 1) * a.do_r + hd) * 2);
-    const u32x4 srdSh = make_srd((w == 0 ? a.lse_in : a.delta) + st0, w < 2 ? (int64_t)s.sq * 4 : 0);
+    const u32x4 srdSh = make_srd((w == 0 ? a.lse2 : a.delta) + st0, w < 2 ? (int64_t)s.sq * 4 : 0);
     auto prefetch = [&](int m, int st, bool real) {
       const uint32_t stage = smem_lds + st * STAGE;
       const uint32_t tq = real ? (uint32_t)(m * BM) * (uint32_t)a.q_r * 2u : (uint32_t)kOffOOB;
@@ -210,7 +210,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
       const float* sDl = sL + BM;
 
-      // LSE / Delta of this lane's 16 query rows.
+      // LSE * log2(e) / Delta of this lane's 16 query rows.
       f32x4 Lr[4], Dr[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -253,7 +253,7 @@ void attn_bwd_dkdv_kernel(Args a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = 4 * jj + r;
-            float p = fast_exp2(__builtin_fmaf(sacc[j], a.scale_log2, -Lr[jj][r] * kLog2e));
+            float p = fast_exp2(__builtin_fmaf(sacc[j], a.scale_log2, -Lr[jj][r]));
             if constexpr (decltype(mask)::value) {
               const int qi = m * BM + 32 * half + 8 * jj + 4 * h + r;
               bool vis = kv_lane < kv0 + rows_k;

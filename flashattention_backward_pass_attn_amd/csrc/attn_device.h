@@ -47,6 +47,7 @@ struct Args {
   const float* lse_in;  // backward input (natural log)
   float* lse_out;       // forward output (natural log)
   float* delta;         // workspace, laid out like lse
+  float* lse2;          // workspace: LSE * log2(e), laid out like lse (written by the preprocess)
   float* delta_out;     // optional copy of delta
   const int32_t* cu_q;
   const int32_t* cu_k;

@@ -94,8 +94,9 @@ attn_status attn_fwd(const attn_params *p, const void *q, const void *k, const v
 
 /*
  * Bytes of device workspace for the fast backward path: Delta, fp32 laid out
- * like lse (the flash-attention CK mha_bwd.cpp page's softmax_d), rounded up
- * to 256 bytes, followed by dS = P o (dP - Delta) in the input dtype as
+ * like lse (the flash-attention CK mha_bwd.cpp page's softmax_d), and
+ * LSE * log2(e) in the same layout, each rounded up to 256 bytes, followed by
+ * dS = P o (dP - Delta) in the input dtype as
  * 32 x 32 tiles (about 2 * Hq * Sq * Sk bytes, independent of `causal`;
  * varlen: bounded by 2 * Hq * total_k * max_seqlen_q plus padding).  With it
  * the dK/dV kernel, which forms dS anyway, stores it and the dQ kernel is a
@@ -106,7 +107,8 @@ attn_status attn_fwd(const attn_params *p, const void *q, const void *k, const v
 attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
 
 /*
- * Bytes of the smallest workspace attn_bwd accepts: Delta only.  With a
+ * Bytes of the smallest workspace attn_bwd accepts: the two row statistics
+ * only.  With a
  * workspace smaller than attn_bwd_workspace_size() (but at least this), the
  * dQ kernel recomputes S, dP and dS per key tile instead of reading them:
  * more arithmetic, no quadratic memory.  Results are identical in value up
