@@ -77,20 +77,33 @@ def kv_head_of(h: int, heads_q: int, heads_kv: int) -> int:
     return h // (heads_q // heads_kv)
 
 
-def visible_mask(sq: int, sk: int, causal: bool) -> np.ndarray:
+def visible_mask(sq: int, sk: int, causal: bool, window=(-1, -1)) -> np.ndarray:
     """Boolean [sq, sk]: True where key j contributes to query i.
 
     Causal follows the tilelang page (``tril``, i.e. keep j <= i) aligned to
-    the bottom-right corner when the lengths differ.
+    the bottom-right corner when the lengths differ.  ``window = (left,
+    right)`` is the local (sliding-window) mask of the CK ``mha_bwd.cpp``
+    page's ``window_size_left`` / ``window_size_right``, also bottom-right
+    aligned (its ``"b:left,right"`` mask): key j is visible to query i iff
+    ``i + (Sk - Sq) - left <= j <= i + (Sk - Sq) + right``, a negative size
+    meaning no bound on that side; causal sets ``right = 0`` as that page
+    does.
     """
-    if not causal:
-        return np.ones((sq, sk), dtype=bool)
+    left, right = window
+    if causal:
+        right = 0
     i = np.arange(sq)[:, None]
     j = np.arange(sk)[None, :]
-    return j <= i + (sk - sq)
+    diag = i + (sk - sq)
+    vis = np.ones((sq, sk), dtype=bool)
+    if right >= 0:
+        vis &= j <= diag + right
+    if left >= 0:
+        vis &= j >= diag - left
+    return vis
 
 
-def head_forward(qh, kh, vh, scale: float, causal: bool):
+def head_forward(qh, kh, vh, scale: float, causal: bool, window=(-1, -1)):
     """One (sequence, query head): qh [Sq,d], kh/vh [Sk,d] -> (O [Sq,d], LSE [Sq]).
 
     tilelang ``ref_program``: scores, mask to -inf, softmax, times V.
@@ -100,7 +113,7 @@ def head_forward(qh, kh, vh, scale: float, causal: bool):
     vh = np.asarray(vh, dtype=np.float64)
     sq, sk = qh.shape[0], kh.shape[0]
     s = scale * (qh @ kh.T)
-    s = np.where(visible_mask(sq, sk, causal), s, -np.inf)
+    s = np.where(visible_mask(sq, sk, causal, window), s, -np.inf)
     if sk == 0:
         m = np.full(sq, -np.inf)
     else:
@@ -115,7 +128,7 @@ def head_forward(qh, kh, vh, scale: float, causal: bool):
     return o, lse
 
 
-def head_backward(qh, kh, vh, doh, scale: float, causal: bool, lse=None):
+def head_backward(qh, kh, vh, doh, scale: float, causal: bool, lse=None, window=(-1, -1)):
     """Gradient of sum(O o dO) for one (sequence, query head).
 
     Returns (dQ [Sq,d], dK [Sk,d], dV [Sk,d], Delta [Sq]).  If ``lse`` is
@@ -128,10 +141,10 @@ def head_backward(qh, kh, vh, doh, scale: float, causal: bool, lse=None):
     doh = np.asarray(doh, dtype=np.float64)
     sq, sk = qh.shape[0], kh.shape[0]
     if lse is None:
-        _, lse = head_forward(qh, kh, vh, scale, causal)
+        _, lse = head_forward(qh, kh, vh, scale, causal, window)
     lse = np.asarray(lse, dtype=np.float64)
     s = scale * (qh @ kh.T)
-    s = np.where(visible_mask(sq, sk, causal), s, -np.inf)
+    s = np.where(visible_mask(sq, sk, causal, window), s, -np.inf)
     p = np.exp(s - lse[:, None])
     dp = doh @ vh.T
     delta = (p * dp).sum(axis=1)
@@ -155,7 +168,7 @@ def _sequences(q, k, cu_seqlens_q, cu_seqlens_k):
 
 
 def attention_forward(q, k, v, scale: float, causal: bool, cu_seqlens_q=None, cu_seqlens_k=None,
-                      heads=None):
+                      heads=None, window=(-1, -1)):
     """Full forward.
 
     Fixed length: q [b,Sq,H,d], k/v [b,Sk,Hk,d] -> O [b,Sq,H,d], LSE [b,H,Sq].
@@ -178,7 +191,7 @@ def attention_forward(q, k, v, scale: float, causal: bool, cu_seqlens_q=None, cu
         oz = selq(o)
         for h in hs:
             g = kv_head_of(h, H, Hk)
-            oh, lh = head_forward(qz[:, h, :], kz[:, g, :], vz[:, g, :], scale, causal)
+            oh, lh = head_forward(qz[:, h, :], kz[:, g, :], vz[:, g, :], scale, causal, window)
             oz[:, h, :] = oh
             if varlen:
                 a = int(np.asarray(cu_seqlens_q)[z])
@@ -189,7 +202,7 @@ def attention_forward(q, k, v, scale: float, causal: bool, cu_seqlens_q=None, cu
 
 
 def attention_backward(q, k, v, do, scale: float, causal: bool, cu_seqlens_q=None,
-                       cu_seqlens_k=None, lse=None, heads=None):
+                       cu_seqlens_k=None, lse=None, heads=None, window=(-1, -1)):
     """Full backward: returns (dQ, dK, dV, Delta) in the layouts of the inputs.
 
     dK/dV of a KV head are summed over the query heads of its group (CK
@@ -225,7 +238,7 @@ def attention_backward(q, k, v, do, scale: float, causal: bool, cu_seqlens_q=Non
             else:
                 lh = np.asarray(lse)[z, h, :]
             dqh, dkh, dvh, dh = head_backward(qz[:, h, :], kz[:, g, :], vz[:, g, :], doz[:, h, :],
-                                              scale, causal, lse=lh)
+                                              scale, causal, lse=lh, window=window)
             dqz[:, h, :] = dqh
             dkz[:, g, :] += dkh
             dvz[:, g, :] += dvh

@@ -77,8 +77,9 @@ def test_hand_worked_examples(ex):
 # ----------------------------------------------------------------------------
 # brute force forward with pure-Python loops (no max shift, direct exp sums)
 # ----------------------------------------------------------------------------
-def _brute_forward(q, k, v, scale, causal):
+def _brute_forward(q, k, v, scale, causal, window=(-1, -1)):
     b, sq, h, d = q.shape
+    wl, wr = window
     sk, hk = k.shape[1], k.shape[2]
     o = np.zeros_like(q)
     lse = np.zeros((b, h, sq))
@@ -90,6 +91,10 @@ def _brute_forward(q, k, v, scale, causal):
                 ws = []
                 for j in range(sk):
                     if causal and j > i + (sk - sq):
+                        continue
+                    if wr >= 0 and j > i + (sk - sq) + wr:
+                        continue
+                    if wl >= 0 and j < i + (sk - sq) - wl:
                         continue
                     s = 0.0
                     for t in range(d):
@@ -130,7 +135,7 @@ def test_forward_matches_brute_force(b, h, hk, sq, sk, d, causal):
 # ----------------------------------------------------------------------------
 # central finite differences of L = sum(O * dO)
 # ----------------------------------------------------------------------------
-def fd_max_rel_error(b, h, hk, sq, sk, d, causal, seed=0, varlen=None, eps=1e-6):
+def fd_max_rel_error(b, h, hk, sq, sk, d, causal, seed=0, varlen=None, eps=1e-6, window=(-1, -1)):
     """Max |numeric - analytic| / max|analytic| over every element of Q, K, V."""
     if varlen is None:
         q, k, v, do = _case(b, h, hk, sq, sk, d, seed)
@@ -140,10 +145,10 @@ def fd_max_rel_error(b, h, hk, sq, sk, d, causal, seed=0, varlen=None, eps=1e-6)
     scale = 1.0 / math.sqrt(d)
 
     def loss(q_, k_, v_):
-        o, _ = oracle.attention_forward(q_, k_, v_, scale, causal, cq, ck)
+        o, _ = oracle.attention_forward(q_, k_, v_, scale, causal, cq, ck, window=window)
         return float((o * do).sum())
 
-    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, scale, causal, cq, ck)
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, scale, causal, cq, ck, window=window)
     worst = 0.0
     for which, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
         num = np.zeros_like(x)
@@ -422,3 +427,96 @@ def test_pins_catch_planted_mask_off_by_one(monkeypatch):
     monkeypatch.setattr(ref, "visible_mask", bad_mask)
     with pytest.raises(AssertionError):
         test_forward_matches_brute_force(1, 4, 2, 6, 6, 3, True)
+
+
+# ----------------------------------------------------------------------------
+# local (sliding-window) mask: the CK mha_bwd.cpp page's window_size_left /
+# window_size_right, bottom-right aligned
+# ----------------------------------------------------------------------------
+WINDOW_CASES = [
+    # b, h, hk, sq, sk, d, causal, (left, right)
+    (1, 2, 2, 9, 9, 4, False, (2, 1)),
+    (1, 2, 1, 7, 7, 3, True, (3, -1)),    # causal + left window
+    (2, 1, 1, 5, 9, 4, False, (1, 3)),    # Sq < Sk
+    (1, 2, 2, 9, 4, 2, False, (0, 2)),    # Sq > Sk: some rows see no key
+    (1, 1, 1, 6, 6, 4, False, (-1, 0)),   # = causal
+    (1, 1, 1, 6, 6, 4, False, (0, -1)),
+]
+
+
+@pytest.mark.parametrize("b,h,hk,sq,sk,d,causal,window", WINDOW_CASES)
+def test_window_forward_matches_brute_force(b, h, hk, sq, sk, d, causal, window):
+    q, k, v, _ = _case(b, h, hk, sq, sk, d, seed=13)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = oracle.attention_forward(q, k, v, scale, causal, window=window)
+    ob, lb = _brute_forward(q, k, v, scale, causal, window)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(np.isinf(lse), np.isinf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("b,h,hk,sq,sk,d,causal,window", WINDOW_CASES[:4])
+def test_window_backward_matches_finite_differences(b, h, hk, sq, sk, d, causal, window):
+    assert fd_max_rel_error(b, h, hk, sq, sk, d, causal, seed=17, window=window) < 1e-7
+
+
+def test_window_special_cases():
+    b, s, h, d = 1, 8, 2, 4
+    q, k, v, do = _case(b, h, h, s, s, d, seed=19)
+    scale = 0.5
+    # (0, 0): every query sees only its own key -> O = V, dQ = dK = 0, dV = dO
+    o, lse = oracle.attention_forward(q, k, v, scale, False, window=(0, 0))
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, scale, False, window=(0, 0))
+    np.testing.assert_allclose(o, v, atol=1e-14)
+    np.testing.assert_allclose(lse, scale * np.einsum("bshd,bshd->bhs", q, k), atol=1e-13)
+    np.testing.assert_allclose(dq, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-14)
+    np.testing.assert_allclose(dv, do, atol=1e-14)
+    # unbounded on both sides = no mask; (-1, 0) = causal; windows wider than
+    # the sequence = no bound
+    for causal, window, same in ((False, (-1, -1), (False, (-1, -1))), (False, (-1, 0), (True, (-1, -1))),
+                                 (False, (s, s), (False, (-1, -1))), (True, (s, 3), (True, (-1, -1)))):
+        a = oracle.attention_backward(q, k, v, do, scale, causal, window=window)
+        r = oracle.attention_backward(q, k, v, do, scale, same[0], window=same[1])
+        for x, y in zip(a, r):
+            np.testing.assert_allclose(x, y, rtol=1e-13, atol=1e-13)
+
+
+def test_window_matches_torch_sdpa_float64():
+    torch = pytest.importorskip("torch")
+    b, h, hk, sq, sk, d = 2, 4, 2, 11, 13, 8
+    wl, wr = 3, 2
+    q, k, v, do = _case(b, h, hk, sq, sk, d, seed=23)
+    scale = d ** -0.5
+    o, _ = oracle.attention_forward(q, k, v, scale, False, window=(wl, wr))
+    dq, dk, dv, _ = oracle.attention_backward(q, k, v, do, scale, False, window=(wl, wr))
+    # the mask written out entry by entry, independently of the oracle
+    m = np.zeros((sq, sk), dtype=bool)
+    for i in range(sq):
+        for j in range(sk):
+            m[i, j] = (i + sk - sq - wl) <= j <= (i + sk - sq + wr)
+    tq, tk, tv = (torch.tensor(x.transpose(0, 2, 1, 3), dtype=torch.float64, requires_grad=True)
+                  for x in (q, k, v))
+    g = h // hk
+    to = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1), attn_mask=torch.tensor(m), scale=scale)
+    to.backward(torch.tensor(do.transpose(0, 2, 1, 3)))
+    np.testing.assert_allclose(o, to.detach().numpy().transpose(0, 2, 1, 3), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy().transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy().transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy().transpose(0, 2, 1, 3), rtol=1e-10, atol=1e-11)
+
+
+def test_pins_catch_planted_window_off_by_one(monkeypatch):
+    real = oracle.attention_ref.visible_mask
+
+    def shifted(sq, sk, causal, window=(-1, -1)):
+        wl, wr = window
+        return real(sq, sk, causal, (wl + 1 if wl >= 0 else wl, wr))
+
+    monkeypatch.setattr(oracle.attention_ref, "visible_mask", shifted)
+    q, k, v, _ = _case(1, 2, 2, 9, 9, 4, seed=13)
+    o, _ = oracle.attention_forward(q, k, v, 0.5, False, window=(2, 1))
+    ob, _ = _brute_forward(q, k, v, 0.5, False, (2, 1))
+    assert np.abs(o - ob).max() > 1e-3
