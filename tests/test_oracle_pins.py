@@ -377,12 +377,12 @@ def test_delta_layout_varlen():
 # mutation test: plausible mistakes planted in the oracle must fail a pin
 # ----------------------------------------------------------------------------
 def _mutant_backward(kind):
-    def hb(qh, kh, vh, doh, scale, causal, lse=None):
+    def hb(qh, kh, vh, doh, scale, causal, lse=None, window=(-1, -1)):
         sq, sk = qh.shape[0], kh.shape[0]
         if lse is None:
-            _, lse = ref.head_forward(qh, kh, vh, scale, causal)
+            _, lse = ref.head_forward(qh, kh, vh, scale, causal, window)
         s = scale * (qh @ kh.T)
-        s = np.where(ref.visible_mask(sq, sk, causal), s, -np.inf)
+        s = np.where(ref.visible_mask(sq, sk, causal, window), s, -np.inf)
         p = np.exp(s - lse[:, None])
         dp = doh @ vh.T
         delta = (p * dp).sum(axis=1)
@@ -418,7 +418,7 @@ def test_pins_catch_planted_gqa_mapping_mistake(monkeypatch):
 
 
 def test_pins_catch_planted_mask_off_by_one(monkeypatch):
-    def bad_mask(sq, sk, causal):
+    def bad_mask(sq, sk, causal, window=(-1, -1)):
         if not causal:
             return np.ones((sq, sk), dtype=bool)
         i = np.arange(sq)[:, None]
