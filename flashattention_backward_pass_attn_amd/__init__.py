@@ -65,6 +65,8 @@ class attn_params(ctypes.Structure):
         ("dq", attn_strides),
         ("dk", attn_strides),
         ("dv", attn_strides),
+        ("window_left", ctypes.c_int32),
+        ("window_right", ctypes.c_int32),
     ]
 
 
@@ -139,8 +141,10 @@ def _ptr(t) -> Optional[int]:
 
 def make_params(q, k, causal: bool, softmax_scale: Optional[float] = None, deterministic: bool = False,
                 cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q: Optional[int] = None,
-                max_seqlen_k: Optional[int] = None) -> attn_params:
-    """Fill attn_params from Q/K tensors.  Strides of the other tensors are set by the callers."""
+                max_seqlen_k: Optional[int] = None, window=(-1, -1)) -> attn_params:
+    """Fill attn_params from Q/K tensors.  Strides of the other tensors are set by the callers.
+
+    ``window = (left, right)``: local attention (see attn_params in include/attn.h), -1 = no bound."""
     varlen = cu_seqlens_q is not None
     p = attn_params()
     p.dtype = _dtype_code(q)
@@ -158,6 +162,7 @@ def make_params(q, k, causal: bool, softmax_scale: Optional[float] = None, deter
     p.softmax_scale = (1.0 / math.sqrt(p.head_dim)) if softmax_scale is None else float(softmax_scale)
     p.causal = 1 if causal else 0
     p.deterministic = 1 if deterministic else 0
+    p.window_left, p.window_right = int(window[0]), int(window[1])
     return p
 
 
@@ -173,7 +178,7 @@ def _check_device(*ts):
 
 
 def attn_fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = None, cu_seqlens_q=None,
-             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, out=None, lse=None):
+             cu_seqlens_k=None, max_seqlen_q=None, max_seqlen_k=None, out=None, lse=None, window=(-1, -1)):
     """O, LSE = attention forward.  Layout [b, s, h, d] (varlen [total, h, d]).
 
     LSE is fp32 natural log, [b, h, Sq] (varlen [h, total_q]).
@@ -182,7 +187,8 @@ def attn_fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = Non
     lib = load_library()
     _check_device(q, k, v)
     varlen = cu_seqlens_q is not None
-    p = make_params(q, k, causal, softmax_scale, False, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k)
+    p = make_params(q, k, causal, softmax_scale, False, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    window)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -208,7 +214,7 @@ def bwd_workspace_size(p: attn_params, minimal: bool = False) -> int:
 def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optional[float] = None,
              deterministic: bool = False, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
              max_seqlen_k=None, dq=None, dk=None, dv=None, workspace=None, return_delta: bool = False,
-             phases: int = PHASE_ALL, minimal_workspace: bool = False):
+             phases: int = PHASE_ALL, minimal_workspace: bool = False, window=(-1, -1)):
     """dQ, dK, dV (and optionally Delta) of sum(O * dO) for attention.
 
     ``phases`` selects which of the three kernels to launch (see attn_bwd_phases
@@ -221,7 +227,7 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optiona
     _check_device(q, k, v, o, lse, dout)
     varlen = cu_seqlens_q is not None
     p = make_params(q, k, causal, softmax_scale, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
-                    max_seqlen_k)
+                    max_seqlen_k, window)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv

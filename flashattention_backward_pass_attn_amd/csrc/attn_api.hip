@@ -51,6 +51,7 @@ attn_status validate_common(const attn_params* p) {
   if (p->head_dim > 128) return ATTN_ERR_UNSUPPORTED;
   if (p->seqlen_q < 0 || p->seqlen_k < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARGUMENT;
+  if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->deterministic != 0 && p->deterministic != 1) return ATTN_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(p->softmax_scale)) return ATTN_ERR_INVALID_ARGUMENT;
   const bool vq = p->cu_seqlens_q != nullptr, vk = p->cu_seqlens_k != nullptr;
@@ -75,6 +76,9 @@ attn_status validate_common(const attn_params* p) {
 }
 
 bool is_varlen(const attn_params* p) { return p->cu_seqlens_q != nullptr; }
+
+// The banded-mask kernels run for causal and for any bounded window side.
+bool banded(const attn_params* p) { return p->causal != 0 || p->window_left >= 0 || p->window_right >= 0; }
 
 // Query-side / key-side tensors may be NULL only when they hold no element.
 bool q_empty(const attn_params* p) { return is_varlen(p) ? p->total_q == 0 : p->seqlen_q == 0; }
@@ -141,6 +145,12 @@ Args make_args(const attn_params* p) {
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * attn::kLog2e;
   a.varlen = vl ? 1 : 0;
+  // banded mask: causal is (no left bound, right bound 0); a side of the
+  // window wider than any offset is no bound
+  const int wr = p->causal ? 0 : p->window_right;
+  const int wl = p->window_left;
+  a.win_l = (wl < 0 || wl >= attn::kWinInf) ? attn::kWinInf : wl;
+  a.win_r = (wr < 0 || wr >= attn::kWinInf) ? attn::kWinInf : wr;
   return a;
 }
 
@@ -237,8 +247,8 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   hipStream_t hs = static_cast<hipStream_t>(stream);
   dim3 grid(p->heads_q * p->batch, (p->seqlen_q + attn::kFwdBM - 1) / attn::kFwdBM, 1);
   const int dt = dtile_for(p->head_dim);
-  if (p->dtype == ATTN_BF16) launch_fwd<true>(a, dt, p->causal, grid, hs);
-  else launch_fwd<false>(a, dt, p->causal, grid, hs);
+  if (p->dtype == ATTN_BF16) launch_fwd<true>(a, dt, banded(p), grid, hs);
+  else launch_fwd<false>(a, dt, banded(p), grid, hs);
   return last_hip_status();
 }
 
@@ -303,7 +313,7 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool bf = p->dtype == ATTN_BF16;
-  const bool causal = p->causal != 0;
+  const bool causal = banded(p);  // causal or local window: the banded kernels
   const int dt = dtile_for(p->head_dim);
   const int qblocks = (p->seqlen_q + attn::kPreRows - 1) / attn::kPreRows;
 

@@ -34,7 +34,7 @@ constexpr int kDqBM = 32 * kDqWaves;     // query rows per dQ workgroup
 constexpr int kDqBN = 64;                // key rows per tile
 constexpr int kDqPD = 6;                 // recompute kernel: LDS reads in flight ahead of their MFMAs
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool BANDED>
 __global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_kernel(Args a) {
   constexpr int NW = kDqWaves;
@@ -67,7 +67,7 @@ void attn_bwd_dq_kernel(Args a) {
   const int hq = blockIdx.x % a.heads_q;
   const int z = blockIdx.x / a.heads_q;
   const Seq s = seq_info(a, z);
-  const int mb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int mb = BANDED ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int q0 = mb * BM;
   if (q0 >= s.sq) return;
   const int hd = a.head_dim;
@@ -76,16 +76,18 @@ void attn_bwd_dq_kernel(Args a) {
   const int qw = q0 + 32 * w;  // first query of this wave
 
   // Key tiles this query block sees.
-  int n_end = (s.sk + BN - 1) / BN;
-  if (CAUSAL) {
-    const int q_last = min(q0 + BM, s.sq) - 1;
-    const int k_lim = q_last + off_causal;
-    n_end = k_lim < 0 ? 0 : min(n_end, k_lim / BN + 1);
+  int n_begin = 0, n_end = (s.sk + BN - 1) / BN;
+  if (BANDED) {
+    const Range kr = band_keys(a, q0, min(q0 + BM, s.sq) - 1, s.sq, s.sk);
+    n_begin = kr.lo / BN;
+    n_end = kr.hi < kr.lo ? n_begin : kr.hi / BN + 1;
   }
-  // Last key this wave's queries see (keys past it are in chunks that may
-  // never have been written).
-  int kw_lim = s.sk - 1;
-  if (CAUSAL) kw_lim = min(kw_lim, qw + 31 + off_causal);
+  // Keys this wave's queries see (chunks wholly outside were never written).
+  int kw_hi = s.sk - 1, kw_lo = -kWinInf;
+  if (BANDED) {
+    kw_hi = min(kw_hi, qw + 31 + off_causal + a.win_r);
+    kw_lo = qw + off_causal - a.win_l;
+  }
 
   f32x16 dq_acc[TD];
 #pragma unroll
@@ -136,9 +138,9 @@ void attn_bwd_dq_kernel(Args a) {
   const int ka = tile_off<CPR>(4 * h + rr, tcol);
   const int kb = tile_off<CPR>(4 * h + rr + 8, tcol);
 
-  if (n_end > 0) prefetch(0);
-  if (n_end > 1) prefetch(1);
-  for (int n = 0; n < n_end; ++n) {
+  if (n_begin < n_end) prefetch(n_begin);
+  if (n_begin + 1 < n_end) prefetch(n_begin + 1);
+  for (int n = n_begin; n < n_end; ++n) {
     if (n + 1 < n_end) {
       wait_vmcnt<KI + SI>();  // tile n landed (tile n+1 may still be in flight)
     } else {
@@ -150,8 +152,8 @@ void attn_bwd_dq_kernel(Args a) {
     const uint8_t* sK = st + DST;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      // this wave's chunk of 32-key tile kt: unwritten if above the diagonal
-      const bool live = n * BN + 32 * kt <= kw_lim;
+      // this wave's chunk of 32-key tile kt: unwritten if outside the band
+      const bool live = n * BN + 32 * kt <= kw_hi && n * BN + 32 * kt + 31 >= kw_lo;
       const uint8_t* chunk = st + (kt * NW + w) * 2048;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -242,7 +244,7 @@ struct DqSchedule {
 // tile is still read in B, hence three LDS stages (3 x 32 KiB at D = 128),
 // filled by direct global->LDS loads one tile ahead.
 // ---------------------------------------------------------------------------
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool BANDED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_recompute_kernel(Args a) {
   constexpr int NW = 8;
@@ -275,7 +277,7 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   const int z = blockIdx.x / a.heads_q;
   const Seq s = seq_info(a, z);
   // Causal blocks near the end of a sequence see the most keys: run them first.
-  const int mb = CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int mb = BANDED ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
   const int q0 = mb * BM;
   if (q0 >= s.sq) return;
   const int hd = a.head_dim;
@@ -334,11 +336,11 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   }
 
   // Key tiles this query block sees.
-  int n_end = (s.sk + BN - 1) / BN;
-  if (CAUSAL) {
-    const int q_last = min(q0 + BM, s.sq) - 1;
-    const int k_lim = q_last + off_causal;
-    n_end = k_lim < 0 ? 0 : min(n_end, k_lim / BN + 1);
+  int n_begin = 0, n_end = (s.sk + BN - 1) / BN;
+  if (BANDED) {
+    const Range kr = band_keys(a, q0, min(q0 + BM, s.sq) - 1, s.sq, s.sk);
+    n_begin = kr.lo / BN;
+    n_end = kr.hi < kr.lo ? n_begin : kr.hi / BN + 1;
   }
   const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
   const uint16_t* vbase = a.v + s.bk * a.v_b + (int64_t)s.k0 * a.v_r + (int64_t)g * a.v_h;
@@ -355,15 +357,22 @@ void attn_bwd_dq_recompute_kernel(Args a) {
       dma16(srdV, vdma[i], stage + KT + S0 * 16);
     }
   };
+  // a tile needs the mask unless every key of it is visible to every query
+  // of this wave
   auto tile_masked = [&](int n) {
-    return (CAUSAL && (n * BN + BN - 1 > qw + off_causal)) || (n * BN + BN > s.sk);
+    return (BANDED && (n * BN + BN - 1 > qw + off_causal + a.win_r || n * BN < qw + 31 + off_causal - a.win_l)) ||
+           (n * BN + BN > s.sk);
   };
 
-  // Last key this lane's query sees, minus the lane's row offset 4*h in the
-  // C layout (keys past the end or above the diagonal are masked).
-  int kv_lim = s.sk - 1;
-  if (CAUSAL) kv_lim = min(kv_lim, qi + off_causal);
-  kv_lim -= 4 * h;
+  // Keys this lane's query sees, minus the lane's row offset 4*h in the C
+  // layout (keys past the end or outside the band are masked).
+  int kv_hi = s.sk - 1, kv_lo = -kWinInf;
+  if (BANDED) {
+    kv_hi = min(kv_hi, qi + off_causal + a.win_r);
+    kv_lo = qi + off_causal - a.win_l;
+  }
+  kv_hi -= 4 * h;
+  kv_lo -= 4 * h;
 
   // Softmax state: sc/pc = current tile's S^T and (dP^T - Delta) per half;
   // the previous tile's half 1 lives in sp/pp until its dS is packed.
@@ -380,7 +389,11 @@ void attn_bwd_dq_recompute_kernel(Args a) {
       // key m*BN + 32*kh + 8*(j/4) + 4*h + j%4: the wave-uniform part
       // against this lane's limit
       const int ks = m * BN + 32 * kh + 8 * (j >> 2) + (j & 3);
-      t = ks <= kv_lim ? t : -__builtin_inff();
+      if (BANDED) {
+        t = (ks <= kv_hi && ks >= kv_lo) ? t : -__builtin_inff();
+      } else {
+        t = ks <= kv_hi ? t : -__builtin_inff();
+      }
     }
     sv[j] = t;
   };
@@ -490,31 +503,40 @@ void attn_bwd_dq_recompute_kernel(Args a) {
     }
   };
 
-  // Tile loop.  The first tile is peeled (no previous half 1), the tiles
-  // that need no mask run in one loop and the masked ones (the diagonal, the
-  // ragged last tile) in a second, so the matrix-core accumulators flow
-  // through straight loops rather than branches.  A wave keeps running
-  // masked tiles past its own last visible key (they add exact zeros) until
-  // the block's last tile, so every wave takes the same barriers.
-  if (n_end > 0) {
-    prefetch(0);
+  // Tile loop.  The first tile is peeled (no previous half 1); the tiles
+  // that need no mask run in one loop and the masked ones (the band's left
+  // edge, its right edge or diagonal, the ragged last tile) in loops of
+  // their own, so the matrix-core accumulators flow through straight loops
+  // rather than branches.  A wave runs every tile of the block (tiles it
+  // cannot see add exact zeros), so every wave takes the same barriers.
+  if (n_begin < n_end) {
+    prefetch(n_begin);
     wait_vmcnt<0>();
     lds_barrier();
-    if (1 < n_end) prefetch(1);
-    if (tile_masked(0)) {
-      run(0, std::true_type{}, std::false_type{}, std::true_type{});
+    if (n_begin + 1 < n_end) prefetch(n_begin + 1);
+    if (tile_masked(n_begin)) {
+      run(n_begin, std::true_type{}, std::false_type{}, std::true_type{});
     } else {
-      run(0, std::true_type{}, std::false_type{}, std::false_type{});
+      run(n_begin, std::true_type{}, std::false_type{}, std::false_type{});
     }
-    int n_um = n_end;  // first tile of this wave that needs the mask
-    if (CAUSAL) {
-      const int lo = qw + off_causal - (BN - 1);  // tiles n with n*BN + BN-1 <= qw + off need none
-      n_um = lo < 0 ? 0 : min(n_um, lo / BN + 1);
+    // this wave's unmasked tiles [u_lo, u_hi): n*BN >= qw + 31 + off - win_l
+    // and n*BN + BN-1 <= qw + off + win_r and n*BN + BN <= sk
+    int u_lo = n_begin + 1, u_hi = min(n_end, s.sk / BN);
+    if (BANDED) {
+      const int lo = qw + 31 + off_causal - a.win_l;
+      if (lo > 0) u_lo = max(u_lo, (lo + BN - 1) / BN);
+      const int hi = qw + off_causal + a.win_r - (BN - 1);
+      u_hi = hi < 0 ? 0 : min(u_hi, hi / BN + 1);
     }
-    n_um = min(n_um, s.sk / BN);
-    n_um = max(n_um, 1);
-    int n = 1;
-    for (; n < n_um; ++n) {
+    int n = n_begin + 1;
+    const int e1 = min(u_lo, n_end);
+    for (; n < e1; ++n) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (n + 1 < n_end) prefetch(n + 1);
+      run(n, std::false_type{}, std::false_type{}, std::true_type{});
+    }
+    for (; n < u_hi; ++n) {
       wait_vmcnt<0>();
       lds_barrier();
       if (n + 1 < n_end) prefetch(n + 1);

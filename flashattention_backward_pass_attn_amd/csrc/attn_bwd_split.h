@@ -41,7 +41,7 @@ constexpr int kDkvBN = 128;   // key rows per dK/dV workgroup
 // swizzled, filled by direct global->LDS loads two tiles ahead) + the P/dS
 // exchange (8 x 4 KiB).
 // ---------------------------------------------------------------------------
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool BANDED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dkdv_kernel(Args a) {
   constexpr int BM = kDkvBM, BN = kDkvBN;
@@ -82,7 +82,7 @@ void attn_bwd_dkdv_kernel(Args a) {
   const int kv0 = nb * BN;
   if (kv0 >= s.sk) return;
   const int hd = a.head_dim;
-  const int off_causal = s.sk - s.sq;  // key j visible to query i iff j <= i + off_causal
+  const int off_causal = s.sk - s.sq;  // banded: key j visible to query i iff |j - (i + off)| in the window
   const int rows_k = min(BN, s.sk - kv0);
 
   // ---- K, V of this wave's 32 key rows as B operands of S = Q K^T and
@@ -138,8 +138,13 @@ void attn_bwd_dkdv_kernel(Args a) {
   }
 
   const int64_t ds_slot = ds_key_slot0(a, z) + 4 * nb + kvg;  // this wave's 32-key tile in dS^T
-  const int m_begin = first_q_block<BM, BN, CAUSAL>(nb, s.sq, s.sk);
-  const int m_end = (s.sq + BM - 1) / BM;
+  // query tiles that see any key of this block
+  int m_begin = 0, m_end = (s.sq + BM - 1) / BM;
+  if (BANDED) {
+    const Range qr = band_queries(a, kv0, kv0 + rows_k - 1, s.sq, s.sk);
+    m_begin = qr.lo / BM;
+    m_end = qr.hi < qr.lo ? m_begin : qr.hi / BM + 1;
+  }
   const int kv_lane = kv0 + 32 * kvg + c32;  // this lane's key column in S / dP
 
   for (int hq = g * a.group; hq < (g + 1) * a.group; ++hq) {
@@ -243,11 +248,23 @@ void attn_bwd_dkdv_kernel(Args a) {
       }
 
       // P and dS.  C layout: lane = key column kv_lane, rows = queries
-      // 32*half + 8*(j/4) + 4*h + j%4.  Tiles crossing the causal diagonal and
+      // 32*half + 8*(j/4) + 4*h + j%4.  Tiles crossing an edge of the band and
       // the partial last key block are masked (zero-filled key rows would
       // otherwise give P = exp(-LSE), which could overflow a 16-bit dS).
-      const bool masked = (CAUSAL && (kv0 + BN - 1 > m * BM + off_causal)) || rows_k < BN;
+      // every (query, key) pair of the tile visible: the lowest query sees
+      // the highest key and the highest query the lowest key
+      const bool masked = (BANDED && (kv0 + BN - 1 > m * BM + off_causal + a.win_r ||
+                                      kv0 < m * BM + BM - 1 + off_causal - a.win_l)) ||
+                          rows_k < BN;
       auto elementwise = [&](auto mask) {
+        // Element (jj, r) is query q_base + e, e = 8*jj + r.  It is visible
+        // iff its key (this lane's) is a real row and e_lo <= e <= e_hi,
+        // from i + off - win_l <= key <= i + off + win_r.
+        const int q_base = m * BM + 32 * half + 4 * h;
+        const int d0 = kv_lane - q_base - off_causal;
+        const int e_lo = BANDED ? d0 - a.win_r : -kWinInf;
+        const int e_hi = BANDED ? d0 + a.win_l : kWinInf;
+        const bool key_ok = kv_lane < kv0 + rows_k;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
@@ -255,10 +272,8 @@ void attn_bwd_dkdv_kernel(Args a) {
             const int j = 4 * jj + r;
             float p = fast_exp2(__builtin_fmaf(sacc[j], a.scale_log2, -Lr[jj][r]));
             if constexpr (decltype(mask)::value) {
-              const int qi = m * BM + 32 * half + 8 * jj + 4 * h + r;
-              bool vis = kv_lane < kv0 + rows_k;
-              if (CAUSAL) vis = vis && (kv_lane <= qi + off_causal);
-              p = vis ? p : 0.f;
+              const int e = 8 * jj + r;
+              p = (key_ok && e >= e_lo && e <= e_hi) ? p : 0.f;
             }
             sacc[j] = p;
             pacc[j] = p * (pacc[j] - Dr[jj][r]);

@@ -65,6 +65,11 @@ struct Args {
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   int32_t varlen;
+  // Banded mask (kernels instantiated with BANDED = true): key j is visible
+  // to query i iff i + off - win_l <= j <= i + off + win_r, off = Sk - Sq
+  // (bottom-right aligned).  Causal: win_l = kWinInf, win_r = 0; a local
+  // window bounds both sides; kWinInf stands for "no bound".
+  int32_t win_l, win_r;
   // dS^T workspace written by the dK/dV kernel and read by the dQ kernel:
   // 2 KiB chunks of 32 keys x 32 queries, chunk (head, key tile, query tile)
   // at ((head * ds_nkt + key tile) * ds_nqt + query tile) * 2048 bytes.
@@ -115,13 +120,21 @@ __device__ inline Seq seq_info(const Args& a, int z) {
   return s;
 }
 
-// First q block (of BM rows) that sees any key of KV block n (of BN rows).
-// Causal visibility is j <= i + (sk - sq).
-template <int BM, int BN, bool CAUSAL>
-__device__ inline int first_q_block(int n, int sq, int sk) {
-  if (!CAUSAL) return 0;
-  int lo = n * BN - (sk - sq);
-  return lo <= 0 ? 0 : lo / BM;
+constexpr int kWinInf = 1 << 29;  // "no bound" for a side of the banded mask
+
+// Keys [lo, hi] (inclusive, clamped to [0, sk-1]; hi < lo when empty) seen by
+// any of the queries [qa, qb] under the banded mask.
+struct Range {
+  int lo, hi;
+};
+__device__ inline Range band_keys(const Args& a, int qa, int qb, int sq, int sk) {
+  const int off = sk - sq;
+  return Range{max(0, qa + off - a.win_l), min(sk - 1, qb + off + a.win_r)};
+}
+// Queries [lo, hi] that see any of the keys [ka, kb].
+__device__ inline Range band_queries(const Args& a, int ka, int kb, int sq, int sk) {
+  const int off = sk - sq;
+  return Range{max(0, ka - off - a.win_r), min(sq - 1, kb - off + a.win_l)};
 }
 
 // ---------------------------------------------------------------------------

@@ -26,7 +26,7 @@ namespace attn {
 constexpr int kFwdBM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kFwdBN = 64;   // key rows per iteration
 
-template <bool BF16, int D, bool CAUSAL>
+template <bool BF16, int D, bool BANDED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(Args a) {
   constexpr int BM = kFwdBM, BN = kFwdBN, LD = D + 8;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hq = blockIdx.x % a.heads_q;
   const int z = blockIdx.x / a.heads_q;
   const Seq s = seq_info(a, z);
-  const int qb0 = (CAUSAL ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y) * BM;
+  const int qb0 = (BANDED ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y) * BM;
   if (qb0 >= s.sq) return;
   const int g = hq / a.group;
   const int hd = a.head_dim;
@@ -70,11 +70,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // Key blocks this query block sees.
-  int n_end = (s.sk + BN - 1) / BN;
-  if (CAUSAL) {
-    const int q_last = min(qb0 + BM, s.sq) - 1;
-    const int k_lim = q_last + (s.sk - s.sq);  // last visible key of the block
-    n_end = k_lim < 0 ? 0 : min(n_end, k_lim / BN + 1);
+  int n_begin = 0, n_end = (s.sk + BN - 1) / BN;
+  if (BANDED) {
+    const Range kr = band_keys(a, qb0, min(qb0 + BM, s.sq) - 1, s.sq, s.sk);
+    n_begin = kr.lo / BN;
+    n_end = kr.hi < kr.lo ? n_begin : kr.hi / BN + 1;
   }
 
   const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   float m_run = -INFINITY, l_run = 0.f;
   const int tr_off = tr_lane_offset(lane, LD);
 
-  if (n_end > 0) load_kv(0);
-  for (int nb = 0; nb < n_end; ++nb) {
+  if (n_begin < n_end) load_kv(n_begin);
+  for (int nb = n_begin; nb < n_end; ++nb) {
     __syncthreads();  // all waves are done with the previous block
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
@@ -132,7 +132,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int j = 0; j < 16; ++j) {
         const int kv = nb * BN + 32 * tk + 8 * (j >> 2) + 4 * h + (j & 3);
         bool vis = kv < s.sk;
-        if (CAUSAL) vis = vis && (kv <= qi + (s.sk - s.sq));
+        if (BANDED) {
+          const int diag = qi + (s.sk - s.sq);
+          vis = vis && kv <= diag + a.win_r && kv >= diag - a.win_l;
+        }
         const float x = vis ? st[tk][j] * a.scale_log2 : -INFINITY;
         st[tk][j] = x;
         mx = fmaxf(mx, x);

@@ -76,6 +76,14 @@ typedef struct {
   int32_t total_q;         /* varlen: cu_seqlens_q[batch] (host copy) */
   int32_t total_k;         /* varlen: cu_seqlens_k[batch] (host copy) */
   attn_strides q, k, v, o, dout, dq, dk, dv;
+  int32_t window_left;     /* local (sliding-window) attention, the CK
+                              mha_bwd.cpp page's window_size_left/right:
+                              key j visible to query i iff
+                              i + (Sk - Sq) - window_left <= j <=
+                              i + (Sk - Sq) + window_right; -1 = no bound on
+                              that side (both -1: no window).  causal = 1
+                              sets window_right = 0, as that page does. */
+  int32_t window_right;
 } attn_params;
 
 /*

@@ -55,7 +55,8 @@ def make_case(dtype, b, h, hk, sq, sk, d, seed, lengths_q=None, lengths_k=None, 
                                  varlen_lengths_q=lengths_q, varlen_lengths_k=lengths_k)
 
 
-def gpu_run(lib, inp, causal, deterministic=False, scale=None, return_delta=True, minimal_workspace=False):
+def gpu_run(lib, inp, causal, deterministic=False, scale=None, return_delta=True, minimal_workspace=False,
+            window=(-1, -1)):
     """Forward then backward on the GPU through the C ABI (fast path, or with
     ``minimal_workspace`` the path whose dQ kernel recomputes dS)."""
     import torch
@@ -69,9 +70,9 @@ def gpu_run(lib, inp, causal, deterministic=False, scale=None, return_delta=True
                   cu_seqlens_k=torch.from_numpy(inp["cu_seqlens_k"]).cuda(),
                   max_seqlen_q=int(inp["lengths_q"].max()) if len(inp["lengths_q"]) else 0,
                   max_seqlen_k=int(inp["lengths_k"].max()) if len(inp["lengths_k"]) else 0)
-    o, lse = lib.attn_fwd(q, k, v, causal=causal, softmax_scale=scale, **kw)
+    o, lse = lib.attn_fwd(q, k, v, causal=causal, softmax_scale=scale, window=window, **kw)
     res = lib.attn_bwd(q, k, v, o, lse, do, causal=causal, softmax_scale=scale, deterministic=deterministic,
-                       return_delta=return_delta, minimal_workspace=minimal_workspace, **kw)
+                       return_delta=return_delta, minimal_workspace=minimal_workspace, window=window, **kw)
     torch.cuda.synchronize()
     out = {"o": o, "lse": lse, "dq": res[0], "dk": res[1], "dv": res[2]}
     if return_delta:
@@ -79,13 +80,14 @@ def gpu_run(lib, inp, causal, deterministic=False, scale=None, return_delta=True
     return out
 
 
-def oracle_run(inp, causal, scale=None, heads=None):
+def oracle_run(inp, causal, scale=None, heads=None, window=(-1, -1)):
     import oracle
     d = inp["q"].shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     cq = inp.get("cu_seqlens_q")
     ck = inp.get("cu_seqlens_k")
-    o, lse = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, causal, cq, ck, heads=heads)
+    o, lse = oracle.attention_forward(inp["q"], inp["k"], inp["v"], scale, causal, cq, ck, heads=heads,
+                                      window=window)
     dq, dk, dv, delta = oracle.attention_backward(inp["q"], inp["k"], inp["v"], inp["do"], scale, causal, cq, ck,
-                                                  heads=heads)
+                                                  heads=heads, window=window)
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": delta}

@@ -55,6 +55,7 @@ def _params(**kw):
     p.heads_q, p.heads_kv, p.head_dim = 8, 2, 64
     p.softmax_scale = 0.125
     p.causal, p.deterministic = 1, 0
+    p.window_left, p.window_right = -1, -1
     for t in ("q", "o", "dout", "dq"):
         setattr(p, t, fa.attn_strides(128 * 8 * 64, 8 * 64, 64))
     for t in ("k", "v", "dk", "dv"):
@@ -85,6 +86,8 @@ def _fwd(clib, p, ptr=FAKE):
     ("seqlen_q", -1, fa.ATTN_ERR_INVALID_ARGUMENT),
     ("causal", 2, fa.ATTN_ERR_INVALID_ARGUMENT),
     ("softmax_scale", float("nan"), fa.ATTN_ERR_INVALID_ARGUMENT),
+    ("window_left", -2, fa.ATTN_ERR_INVALID_ARGUMENT),
+    ("window_right", -5, fa.ATTN_ERR_INVALID_ARGUMENT),
 ])
 def test_invalid_parameters_rejected(clib, field, value, expect):
     p = _params(**{field: value})

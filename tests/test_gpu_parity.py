@@ -76,6 +76,29 @@ def test_small_parity_minimal_workspace(lib, case):
     _compare(out, ref, case[1])
 
 
+# local (sliding-window) attention: name, dtype, b, h, hk, sq, sk, d, causal, lens, (left, right)
+WINDOW_CASES = [
+    ("window_fp16_l100_r30_d64", "fp16", 1, 2, 2, 300, 300, 64, False, None, (100, 30)),
+    ("window_bf16_causal_l150_d128", "bf16", 2, 4, 2, 333, 333, 128, True, None, (150, -1)),
+    ("window_bf16_sq_lt_sk_l0_r70_d128", "bf16", 1, 2, 1, 90, 260, 128, False, None, (0, 70)),
+    ("window_fp16_sq_gt_sk_l40_r0_d64", "fp16", 1, 2, 2, 270, 100, 64, False, None, (40, 0)),
+    ("window_fp16_left_only_d96", "fp16", 1, 2, 2, 200, 200, 96, False, None, (70, -1)),
+    ("window_bf16_varlen_l64_r64_d128", "bf16", 3, 2, 2, 0, 0, 128, False, ([300, 17, 129], [300, 17, 129]), (64, 64)),
+    ("window_fp16_tiny_l0_r0_d32", "fp16", 1, 2, 2, 100, 100, 32, False, None, (0, 0)),
+]
+
+
+@pytest.mark.parametrize("minimal", [False, True], ids=["stored_ds", "recompute"])
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def test_window_parity(lib, case, minimal):
+    print(f"[gpu] window parity {case[0]} minimal={minimal}", flush=True)
+    inp = _inputs(case[:10], seed=2024)
+    causal, window = case[8], case[10]
+    out = gpu_run(lib, inp, causal, minimal_workspace=minimal, window=window)
+    ref = oracle_run(inp, causal, window=window)
+    _compare(out, ref, case[1])
+
+
 def test_both_workspace_paths_agree(lib):
     """dK, dV identical; dQ within the rounding of the same operations."""
     print("[gpu] fast vs minimal workspace, ragged causal bf16 d128", flush=True)
