@@ -53,7 +53,7 @@ attn_status validate_common(const attn_params* p) {
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->deterministic != 0 && p->deterministic != 1) return ATTN_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(p->softmax_scale)) return ATTN_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.f)) return ATTN_ERR_INVALID_ARGUMENT;
   const bool vq = p->cu_seqlens_q != nullptr, vk = p->cu_seqlens_k != nullptr;
   if (vq != vk) return ATTN_ERR_INVALID_ARGUMENT;
   if (vq && (p->total_q < 0 || p->total_k < 0)) return ATTN_ERR_INVALID_ARGUMENT;

@@ -54,8 +54,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int g = hq / a.group;
   const int hd = a.head_dim;
 
-  // This lane's query row (a column of S^T).
-  const int qi = qb0 + 32 * w + c32;
+  // This lane's query row (a column of S^T); the wave's first query.
+  const int qw = qb0 + 32 * w;
+  const int qi = qw + c32;
+  const int off = s.sk - s.sq;  // bottom-right alignment of the band
   const bool q_ok = qi < s.sq;
 
   // Q as the B operand of S^T = K Q^T: column qi, k = head dim.
@@ -124,24 +126,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
 
-    // Scale into the exp2 domain, mask, row max over keys.
+    // Mask (only on tiles crossing an edge of the band or the last key),
+    // row max over keys, exp2 with scale*log2(e) folded into the fma.
+    // Masked scores become -inf; max(scale*log2e*s) = scale*log2e*max(s).
+    const bool masked = (BANDED && (nb * BN + BN - 1 > qw + off + a.win_r || nb * BN < qw + 31 + off - a.win_l)) ||
+                        nb * BN + BN > s.sk;
+    if (masked) {
+      const int kv_hi = min(s.sk - 1, BANDED ? qi + off + a.win_r : s.sk - 1) - 4 * h;
+      const int kv_lo = (BANDED ? qi + off - a.win_l : -kWinInf) - 4 * h;
+#pragma unroll
+      for (int tk = 0; tk < TK; ++tk) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int ks = nb * BN + 32 * tk + 8 * (j >> 2) + (j & 3);  // key minus the lane's 4*h
+          st[tk][j] = (ks <= kv_hi && ks >= kv_lo) ? st[tk][j] : -INFINITY;
+        }
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int tk = 0; tk < TK; ++tk) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kv = nb * BN + 32 * tk + 8 * (j >> 2) + 4 * h + (j & 3);
-        bool vis = kv < s.sk;
-        if (BANDED) {
-          const int diag = qi + (s.sk - s.sq);
-          vis = vis && kv <= diag + a.win_r && kv >= diag - a.win_l;
-        }
-        const float x = vis ? st[tk][j] * a.scale_log2 : -INFINITY;
-        st[tk][j] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[tk][j]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int tk = 0; tk < TK; ++tk) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(st[tk][j] - m_use);
+        const float p = fast_exp2(__builtin_fmaf(st[tk][j], a.scale_log2, -m_use));
         st[tk][j] = p;
         ls += p;
       }

@@ -66,7 +66,8 @@ typedef struct {
   int32_t heads_q;         /* H > 0 */
   int32_t heads_kv;        /* Hk > 0, H % Hk == 0 */
   int32_t head_dim;        /* d % 8 == 0; d in {64, 96, 128} is built */
-  float softmax_scale;     /* scores are scale * Q K^T; pass 1/sqrt(d) */
+  float softmax_scale;     /* scores are scale * Q K^T, scale > 0 (finite);
+                              pass 1/sqrt(d) for the default */
   int32_t causal;          /* 0/1; key j visible to query i iff
                               j <= i + (Sk - Sq) (bottom-right aligned) */
   int32_t deterministic;   /* bwd: 1 = bit-identical run to run (always

@@ -86,6 +86,8 @@ def _fwd(clib, p, ptr=FAKE):
     ("seqlen_q", -1, fa.ATTN_ERR_INVALID_ARGUMENT),
     ("causal", 2, fa.ATTN_ERR_INVALID_ARGUMENT),
     ("softmax_scale", float("nan"), fa.ATTN_ERR_INVALID_ARGUMENT),
+    ("softmax_scale", -0.5, fa.ATTN_ERR_INVALID_ARGUMENT),
+    ("softmax_scale", 0.0, fa.ATTN_ERR_INVALID_ARGUMENT),
     ("window_left", -2, fa.ATTN_ERR_INVALID_ARGUMENT),
     ("window_right", -5, fa.ATTN_ERR_INVALID_ARGUMENT),
 ])
