@@ -17,7 +17,7 @@ one untimed forward.  Prints ONE JSON line on stdout:
   cpu_baseline         the fp64 CPU oracle's backward on a bounded sample of
                        the same workload (a few heads), scaled to TFLOP/s.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 40] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -182,8 +182,8 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, command: str) -
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default=workloads.DEFAULT_BENCH_WORKLOAD, choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
