@@ -65,7 +65,10 @@ typedef struct {
   int32_t seqlen_k;        /* fixed-length Sk (>= 0); varlen: max length */
   int32_t heads_q;         /* H > 0 */
   int32_t heads_kv;        /* Hk > 0, H % Hk == 0 */
-  int32_t head_dim;        /* d % 8 == 0; d in {64, 96, 128} is built */
+  int32_t head_dim;        /* d % 8 == 0, d <= 256; d <= 128 is built (each
+                              head is computed in a 64- or 128-wide tile,
+                              zero-padded); 136..256 gives
+                              ATTN_ERR_UNSUPPORTED */
   float softmax_scale;     /* scores are scale * Q K^T, scale > 0 (finite);
                               pass 1/sqrt(d) for the default */
   int32_t causal;          /* 0/1; key j visible to query i iff
@@ -86,6 +89,20 @@ typedef struct {
                               sets window_right = 0, as that page does. */
   int32_t window_right;
 } attn_params;
+
+/*
+ * Limits of this build, reported as ATTN_ERR_UNSUPPORTED before any launch
+ * (the arguments are valid for the method):
+ *   head_dim above 128;
+ *   heads_q or batch above 65535, or heads_q * batch above 2^31 - 1;
+ *   seqlen_q or seqlen_k above 65535 * 64;
+ *   a per-head extent of 1 GiB or more: seqlen * row stride * 2 bytes, for
+ *     any of q, o, dout, dq (seqlen_q) or k, v, dk, dv (seqlen_k) -- the
+ *     kernels address one head of one sequence with 32-bit byte offsets;
+ *   a row or head stride that is not positive; a batch, row or head
+ *     stride, or a tensor address, that is not a multiple of 8 elements
+ *     (16 bytes).
+ */
 
 /*
  * Forward: O = softmax(scale * Q K^T, masked) V and LSE (natural log).
