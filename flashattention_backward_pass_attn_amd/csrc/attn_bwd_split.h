@@ -34,9 +34,10 @@ constexpr int kDkvBN = 128;   // key rows per dK/dV workgroup
 // ---------------------------------------------------------------------------
 // dK / dV: one workgroup per (128-key block, KV head, sequence), looping over
 // the query blocks (and, for GQA, over the query heads of the KV head).
-//   wave w: key rows 32*(w&3) .. +32 of the block; query half (w>>2) of each
-//   64-query tile for S = Q K^T and dP = dO V^T; head-dim half (w>>2) for
-//   dV += P^T dO and dK += dS^T Q.
+//   wave w: key rows 32*(w>>1) .. +32 of the block, shared with its partner
+//   w^1; query half (w&1) of each 64-query tile for S = Q K^T and
+//   dP = dO V^T; head-dim half (w&1) for dV += P^T dO and dK += dS^T Q.
+//   Waves 0-3 and 4-7 (one of each on every SIMD) run half a tile apart.
 // LDS (D = 128): three stages of {Q, dO, LSE, Delta} (3 x 32.5 KiB,
 // swizzled, filled by direct global->LDS loads two tiles ahead) + the P/dS
 // exchange (8 x 4 KiB).
@@ -64,8 +65,9 @@ void attn_bwd_dkdv_kernel(Args a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_id();
-  const int kvg = w & 3;          // key-row group of this wave
-  const int half = w >> 2;        // query half (S, dP) and head-dim half (dV, dK)
+  const int kvg = w >> 1;         // key-row group of this wave (a pair of waves)
+  const int half = w & 1;         // query half (S, dP) and head-dim half (dV, dK)
+  const int grp = w >> 2;         // pipeline group: 0 runs half a tile ahead of 1
   const int h = lane >> 5;
   const int c32 = lane & 31;
   const int sl = lane & 15;
@@ -122,7 +124,7 @@ void attn_bwd_dkdv_kernel(Args a) {
     tb[t] = tile_off<CPR>(4 * h + rr + 8, col);
   }
   uint8_t* const xown = smem + NSTAGE * STAGE + w * XB + lane * 16;
-  const uint8_t* const xpar = smem + NSTAGE * STAGE + (w ^ 4) * XB + lane * 16;
+  const uint8_t* const xpar = smem + NSTAGE * STAGE + (w ^ 1) * XB + lane * 16;
 
   auto slot_off = [&](int S, int row_stride) {
     const int r = S / CPR;
@@ -147,12 +149,16 @@ void attn_bwd_dkdv_kernel(Args a) {
   }
   const int kv_lane = kv0 + 32 * kvg + c32;  // this lane's key column in S / dP
 
+  // Packed P^T / dS^T operands of this wave's 32 queries, formed in phase 1
+  // of a tile and consumed in its phase 2 (for the second group, across the
+  // loop's back edge).
+  u32x4 pf[2], dsf[2];
+
   for (int hq = g * a.group; hq < (g + 1) * a.group; ++hq) {
     if (m_begin >= m_end) break;
     const uint16_t* qb = a.q + s.bq * a.q_b + (int64_t)s.q0 * a.q_r + (int64_t)hq * a.q_h;
     const uint16_t* db = a.dout + s.bq * a.do_b + (int64_t)s.q0 * a.do_r + (int64_t)hq * a.do_h;
     const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h;
-    // this wave's row of dS^T chunks for query head hq (query tile qt at + qt * 2 KiB)
     // this wave's row of dS^T chunks for query head hq (query tile qt at + qt * 2 KiB)
     const uint8_t* ds_head = reinterpret_cast<const uint8_t*>(a.ds) +
                              ((int64_t)hq * a.ds_nkt + ds_slot) * (int64_t)a.ds_nqt * 2048;
@@ -186,45 +192,21 @@ void attn_bwd_dkdv_kernel(Args a) {
       dma4(srdSh, (int)(real ? (uint32_t)(m * BM + lane) * 4u : (uint32_t)kOffOOB), sdst);
     };
 
-    // Before refilling stage 0 for a new head, every wave must be done with
-    // the previous head's last tile.
-    if (hq != g * a.group) lds_barrier();
-    prefetch(m_begin, 0, true);
-    prefetch(m_begin + 1, 1, m_begin + 1 < m_end);
-    {
-      // two empty stores stand in for the previous tile's dS^T stores, so
-      // the wait at the end of every tile counts the same operations
-      const rsrc_t none = make_rsrc(a.q, 0);
-      buf_store128_nt(none, 0, u32x4{0u, 0u, 0u, 0u});
-      buf_store128_nt(none, 16, u32x4{0u, 0u, 0u, 0u});
-    }
-    wait_vmcnt<NPF + 2>();  // tile m_begin landed
-    lds_barrier();
-    int st = 0;
-    for (int m = m_begin; m < m_end; ++m) {
-      // stage (st + 2) % 3 was last read in the previous tile, which every
-      // wave has finished (barrier at the end of the loop body)
-      const int st2 = st == 0 ? 2 : st - 1;
-      prefetch(m + 2, st2, m + 2 < m_end);
-
+    // Phase 1 of tile m (stage st): S and dP for this wave's 32 queries x 32
+    // keys, P and dS, the packed operands into the exchange slot and dS^T to
+    // the workspace.
+    auto phase1 = [&](int m, int st) {
       const uint8_t* sQ = smem + st * STAGE;
       // per-tile base (stage offsets leave the chunk bits alone), so the
       // per-step XORs are not hoisted out of the loop into 8 registers
       const int svn = svb + st * STAGE;
-      const uint8_t* sdO = sQ + TILE;
       const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
       const float* sDl = sL + BM;
 
-      // LSE * log2(e) / Delta of this lane's 16 query rows.
-      f32x4 Lr[4], Dr[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int qr = 32 * half + 8 * jj + 4 * h;
-        Lr[jj] = *reinterpret_cast<const f32x4*>(sL + qr);
-        Dr[jj] = *reinterpret_cast<const f32x4*>(sDl + qr);
-      }
-
       // S = Q K^T and dP = dO V^T: 32 queries (this wave's half) x 32 keys.
+      // These products go out at raised priority: the other wave on this
+      // SIMD is in phase 2 (matrix-core work only), and the sooner these
+      // finish, the more of this wave's softmax runs under its products.
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       {
         constexpr int NS = D / 16, PD = 3;
@@ -234,6 +216,7 @@ void attn_bwd_dkdv_kernel(Args a) {
           fo[slot] = lds_rd128(smem, (svn ^ (32 * sd)) + TILE);
         };
         sched_fence();
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < PD; ++i) rd(i, i);
         sched_fence();
@@ -245,6 +228,18 @@ void attn_bwd_dkdv_kernel(Args a) {
           pacc = mfma32<BF16>(a1, vf[sd], pacc);
           sched_fence();
         }
+        __builtin_amdgcn_s_setprio(0);
+        sched_fence();
+      }
+
+      // LSE * log2(e) / Delta of this lane's 16 query rows, read while the
+      // last products drain (not held in registers across them).
+      f32x4 Lr[4], Dr[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int qr = 32 * half + 8 * jj + 4 * h;
+        Lr[jj] = *reinterpret_cast<const f32x4*>(sL + qr);
+        Dr[jj] = *reinterpret_cast<const f32x4*>(sDl + qr);
       }
 
       // P and dS.  C layout: lane = key column kv_lane, rows = queries
@@ -288,7 +283,6 @@ void attn_bwd_dkdv_kernel(Args a) {
 
       // P^T and dS^T as A operands (row = key, k = query): k-slot i of 16-query
       // step s2 is query 16*s2 + 8*(i/4) + 4*h + i%4 of this wave's half.
-      u32x4 pf[2], dsf[2];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
@@ -297,7 +291,7 @@ void attn_bwd_dkdv_kernel(Args a) {
           dsf[s2][e] = pack2<BF16>(pacc[8 * s2 + 2 * e], pacc[8 * s2 + 2 * e + 1]);
         }
       }
-      // Trade with the partner wave (same keys, other query half).
+      // For the partner wave (same keys, other query half).
       *reinterpret_cast<u32x4*>(xown + 0 * 1024) = pf[0];
       *reinterpret_cast<u32x4*>(xown + 1 * 1024) = pf[1];
       *reinterpret_cast<u32x4*>(xown + 2 * 1024) = dsf[0];
@@ -316,48 +310,94 @@ void attn_bwd_dkdv_kernel(Args a) {
         buf_store128_nt(rS, c32 * 64 + h * 32, dsf[0]);
         buf_store128_nt(rS, c32 * 64 + h * 32 + 16, dsf[1]);
       }
-      lds_barrier();
+    };
+
+    // Phase 2 of tile m (stage st): dV += P^T dO and dK += dS^T Q over all
+    // 64 queries of the tile, for this wave's head-dim half, with the
+    // partner's operands from the exchange slot (written before the barrier
+    // that ends phase 1).  Step = (query half qh, s2, t).
+    auto phase2 = [&](int st) {
+      const uint8_t* sQ = smem + st * STAGE;
+      const uint8_t* sdO = sQ + TILE;
       u32x4 ppf[2], pdsf[2];
       ppf[0] = *reinterpret_cast<const u32x4*>(xpar + 0 * 1024);
       ppf[1] = *reinterpret_cast<const u32x4*>(xpar + 1 * 1024);
       pdsf[0] = *reinterpret_cast<const u32x4*>(xpar + 2 * 1024);
       pdsf[1] = *reinterpret_cast<const u32x4*>(xpar + 3 * 1024);
-
-      // dV += P^T dO and dK += dS^T Q over all 64 queries of the tile, for
-      // this wave's head-dim half.  Step = (query half qh, s2, t).
-      {
-        constexpr int NS = 4 * TDH, PD = 2;
-        u32x4 fo[PD], fq[PD];
-        auto rd = [&](int i, int slot) {
-          const int kstep = i / TDH, t = i % TDH;
-          const int qh = (kstep < 2) ? half : (half ^ 1);
-          const int ro = (32 * qh + 16 * (kstep & 1)) * RB;
-          fo[slot] = tr_frag_b(sdO, ro + ta[t], ro + tb[t]);
-          fq[slot] = tr_frag_b(sQ, ro + ta[t], ro + tb[t]);
-        };
-        sched_fence();
+      constexpr int NS = 4 * TDH, PD = 2;
+      u32x4 fo[PD], fq[PD];
+      auto rd = [&](int i, int slot) {
+        const int kstep = i / TDH, t = i % TDH;
+        const int qh = (kstep < 2) ? half : (half ^ 1);
+        const int ro = (32 * qh + 16 * (kstep & 1)) * RB;
+        fo[slot] = tr_frag_b(sdO, ro + ta[t], ro + tb[t]);
+        fq[slot] = tr_frag_b(sQ, ro + ta[t], ro + tb[t]);
+      };
+      sched_fence();
 #pragma unroll
-        for (int i = 0; i < PD; ++i) rd(i, i);
-        sched_fence();
+      for (int i = 0; i < PD; ++i) rd(i, i);
+      sched_fence();
 #pragma unroll
-        for (int i = 0; i < NS; ++i) {
-          const int kstep = i / TDH, t = i % TDH;
-          const u32x4 bo = fo[i % PD], bq = fq[i % PD];
-          if (i + PD < NS) rd(i + PD, i % PD);
-          const u32x4 ap = kstep < 2 ? pf[kstep] : ppf[kstep - 2];
-          const u32x4 ad = kstep < 2 ? dsf[kstep] : pdsf[kstep - 2];
-          dv_acc[t] = mfma32<BF16>(ap, bo, dv_acc[t]);
-          dk_acc[t] = mfma32<BF16>(ad, bq, dk_acc[t]);
-          sched_fence();
-        }
+      for (int i = 0; i < NS; ++i) {
+        const int kstep = i / TDH, t = i % TDH;
+        const u32x4 bo = fo[i % PD], bq = fq[i % PD];
+        if (i + PD < NS) rd(i + PD, i % PD);
+        const u32x4 ap = kstep < 2 ? pf[kstep] : ppf[kstep - 2];
+        const u32x4 ad = kstep < 2 ? dsf[kstep] : pdsf[kstep - 2];
+        dv_acc[t] = mfma32<BF16>(ap, bo, dv_acc[t]);
+        dk_acc[t] = mfma32<BF16>(ad, bq, dk_acc[t]);
+        sched_fence();
       }
-      // Tile m+1 landed.  Issued after its loads: the previous tile's two
-      // dS^T stores, tile m+2's loads and this tile's two stores, which may
-      // all stay in flight (the counter retires in order).
-      wait_vmcnt<NPF + 4>();
-      lds_barrier();  // everyone's loads; all reads of this stage retired
-      st = st == 2 ? 0 : st + 1;
+    };
+
+    // Two groups of four waves (two pairs each) run half a tile apart: in
+    // every interval between barriers one wave of each SIMD is in phase 1
+    // (products, then the softmax on the vector ALU) and the other in phase
+    // 2 (products only), so the softmax of one overlaps the other's matrix
+    // work.  Both groups run the same straight loop body, phase 1, barrier,
+    // phase 2, barrier; group 1 enters it one barrier late (s_barrier counts
+    // arrivals, not program locations) and group 0 passes one extra barrier
+    // at the end, so interval k holds group 0's phase (k & 1) of tile k / 2
+    // and group 1's phase ((k - 1) & 1) of tile (k - 1) / 2.
+    // Tile j (relative) lives in stage j % 3.  Tile j + 2 is loaded at the
+    // start of interval 2j + 1 (group 0's phase 2 of tile j, group 1's phase
+    // 1), after the barrier that ends the last read of its stage (group 1's
+    // phase 2 of tile j - 1), and this wave's share of tile j + 1 is waited
+    // for at the end of interval 2j + 1, before group 0 reads it.
+    //
+    // Memory-counter accounting: after tile j + 1's loads a group-0 wave
+    // issues two dS^T stores (phase 1 of tile j) and tile j + 2's loads; a
+    // group-1 wave issues the stores of tile j - 1, tile j + 2's loads and the
+    // stores of tile j.  Two empty stores stand in for tile -1's.
+    const int n = m_end - m_begin;
+    // The previous head's last interval ended with a barrier: every wave is
+    // done with its stages.
+    prefetch(m_begin, 0, true);
+    prefetch(m_begin + 1, 1, n > 1);
+    if (grp) {
+      const rsrc_t none = make_rsrc(a.q, 0);
+      buf_store128_nt(none, 0, u32x4{0u, 0u, 0u, 0u});
+      buf_store128_nt(none, 16, u32x4{0u, 0u, 0u, 0u});
+      wait_vmcnt<NPF + 2>();
+    } else {
+      wait_vmcnt<NPF>();
     }
+    lds_barrier();  // tile 0 landed
+    if (grp) lds_barrier();  // interval 0: group 0's phase 1 of tile 0
+    int st = 0, st_load = 2;
+    for (int j = 0; j < n; ++j) {
+      if (grp) prefetch(m_begin + j + 2, st_load, j + 2 < n);
+      phase1(m_begin + j, st);
+      if (grp) wait_vmcnt<NPF + 4>();
+      lds_barrier();  // exchange slots written
+      if (!grp) prefetch(m_begin + j + 2, st_load, j + 2 < n);
+      phase2(st);
+      if (!grp) wait_vmcnt<NPF + 2>();
+      lds_barrier();  // loads published; stage reads retired
+      st = st == 2 ? 0 : st + 1;
+      st_load = st_load == 2 ? 0 : st_load + 1;
+    }
+    if (!grp) lds_barrier();  // interval 2n: group 1's phase 2 of the last tile
   }
 
   // ---- Epilogue: dK * scale, dV; convert (round to nearest even) and store.
