@@ -195,7 +195,7 @@ void attn_bwd_dkdv_kernel(Args a) {
     // Phase 1 of tile m (stage st): S and dP for this wave's 32 queries x 32
     // keys, P and dS, the packed operands into the exchange slot and dS^T to
     // the workspace.
-    auto phase1 = [&](int m, int st) {
+    auto phase1_body = [&](int m, int st, auto mask) {
       const uint8_t* sQ = smem + st * STAGE;
       // per-tile base (stage offsets leave the chunk bits alone), so the
       // per-step XORs are not hoisted out of the loop into 8 registers
@@ -203,17 +203,46 @@ void attn_bwd_dkdv_kernel(Args a) {
       const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
       const float* sDl = sL + BM;
 
-      // S = Q K^T and dP = dO V^T: 32 queries (this wave's half) x 32 keys.
-      // These products go out at raised priority: the other wave on this
-      // SIMD is in phase 2 (matrix-core work only), and the sooner these
-      // finish, the more of this wave's softmax runs under its products.
+      // LSE * log2(e) of this lane's 16 query rows (needed right after the S
+      // products); Delta is read under the dP products.
+      f32x4 Lr[4], Dr[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) Lr[jj] = *reinterpret_cast<const f32x4*>(sL + 32 * half + 8 * jj + 4 * h);
+
+      // Visibility of the tile's (query, key) pairs (masked tiles only).
+      // C layout of S / dP: lane = key column kv_lane, rows = queries
+      // 32*half + 8*(j/4) + 4*h + j%4.  Element (jj, r) is query q_base + e, e = 8*jj + r.  It is visible iff
+      // its key (this lane's) is a real row and e_lo <= e <= e_hi, from
+      // i + off - win_l <= key <= i + off + win_r.
+      const int q_base = m * BM + 32 * half + 4 * h;
+      const int d0 = kv_lane - q_base - off_causal;
+      const int e_lo = BANDED ? d0 - a.win_r : -kWinInf;
+      const int e_hi = BANDED ? d0 + a.win_l : kWinInf;
+      const bool key_ok = kv_lane < kv0 + rows_k;
+
+      // S = Q K^T, then dP = dO V^T: 32 queries (this wave's half) x 32
+      // keys, one chain after the other, so that P = exp2(S*scale*log2e -
+      // LSE2) runs on the vector ALU under the dP products.  The products go
+      // out at raised priority: the other wave on this SIMD is in phase 2
+      // (matrix-core work only) and fills the gaps.
       f32x16 sacc = f32x16{}, pacc = f32x16{};
       {
         constexpr int NS = D / 16, PD = 3;
-        u32x4 fq[PD], fo[PD];
-        auto rd = [&](int sd, int slot) {
-          fq[slot] = lds_rd128(smem, svn ^ (32 * sd));
-          fo[slot] = lds_rd128(smem, (svn ^ (32 * sd)) + TILE);
+        static_assert(16 % NS == 0, "P elements spread evenly over the dP products");
+        u32x4 fr[PD];
+        // operand step i: Q for i < NS (S chain), dO for i >= NS (dP chain)
+        auto rd = [&](int i, int slot) {
+          const int sd = i % NS;
+          fr[slot] = lds_rd128(smem, (svn ^ (32 * sd)) + (i < NS ? 0 : TILE));
+        };
+        auto p_elem = [&](int j) {
+          const int jj = j / 4, r = j % 4;
+          float p = fast_exp2(__builtin_fmaf(sacc[j], a.scale_log2, -Lr[jj][r]));
+          if constexpr (decltype(mask)::value) {
+            const int e = 8 * jj + r;
+            p = (key_ok && e >= e_lo && e <= e_hi) ? p : 0.f;
+          }
+          sacc[j] = p;
         };
         sched_fence();
         __builtin_amdgcn_s_setprio(1);
@@ -221,65 +250,30 @@ void attn_bwd_dkdv_kernel(Args a) {
         for (int i = 0; i < PD; ++i) rd(i, i);
         sched_fence();
 #pragma unroll
-        for (int sd = 0; sd < NS; ++sd) {
-          const u32x4 a0 = fq[sd % PD], a1 = fo[sd % PD];
-          if (sd + PD < NS) rd(sd + PD, sd % PD);
-          sacc = mfma32<BF16>(a0, kf[sd], sacc);
-          pacc = mfma32<BF16>(a1, vf[sd], pacc);
+        for (int i = 0; i < 2 * NS; ++i) {
+          const u32x4 op = fr[i % PD];
+          if (i + PD < 2 * NS) rd(i + PD, i % PD);
+          if (i < NS) {
+            sacc = mfma32<BF16>(op, kf[i], sacc);
+          } else {
+            pacc = mfma32<BF16>(op, vf[i - NS], pacc);
+            if (i == NS + 1) {
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) Dr[jj] = *reinterpret_cast<const f32x4*>(sDl + 32 * half + 8 * jj + 4 * h);
+            }
+            // 16 / NS elements of P per dP product
+            constexpr int EPP = 16 / NS;
+#pragma unroll
+            for (int e = 0; e < EPP; ++e) p_elem(EPP * (i - NS) + e);
+          }
           sched_fence();
         }
         __builtin_amdgcn_s_setprio(0);
         sched_fence();
       }
-
-      // LSE * log2(e) / Delta of this lane's 16 query rows, read while the
-      // last products drain (not held in registers across them).
-      f32x4 Lr[4], Dr[4];
+      // dS = P o (dP - Delta)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int qr = 32 * half + 8 * jj + 4 * h;
-        Lr[jj] = *reinterpret_cast<const f32x4*>(sL + qr);
-        Dr[jj] = *reinterpret_cast<const f32x4*>(sDl + qr);
-      }
-
-      // P and dS.  C layout: lane = key column kv_lane, rows = queries
-      // 32*half + 8*(j/4) + 4*h + j%4.  Tiles crossing an edge of the band and
-      // the partial last key block are masked (zero-filled key rows would
-      // otherwise give P = exp(-LSE), which could overflow a 16-bit dS).
-      // every (query, key) pair of the tile visible: the lowest query sees
-      // the highest key and the highest query the lowest key
-      const bool masked = (BANDED && (kv0 + BN - 1 > m * BM + off_causal + a.win_r ||
-                                      kv0 < m * BM + BM - 1 + off_causal - a.win_l)) ||
-                          rows_k < BN;
-      auto elementwise = [&](auto mask) {
-        // Element (jj, r) is query q_base + e, e = 8*jj + r.  It is visible
-        // iff its key (this lane's) is a real row and e_lo <= e <= e_hi,
-        // from i + off - win_l <= key <= i + off + win_r.
-        const int q_base = m * BM + 32 * half + 4 * h;
-        const int d0 = kv_lane - q_base - off_causal;
-        const int e_lo = BANDED ? d0 - a.win_r : -kWinInf;
-        const int e_hi = BANDED ? d0 + a.win_l : kWinInf;
-        const bool key_ok = kv_lane < kv0 + rows_k;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 4 * jj + r;
-            float p = fast_exp2(__builtin_fmaf(sacc[j], a.scale_log2, -Lr[jj][r]));
-            if constexpr (decltype(mask)::value) {
-              const int e = 8 * jj + r;
-              p = (key_ok && e >= e_lo && e <= e_hi) ? p : 0.f;
-            }
-            sacc[j] = p;
-            pacc[j] = p * (pacc[j] - Dr[jj][r]);
-          }
-        }
-      };
-      if (masked) {
-        elementwise(std::true_type{});
-      } else {
-        elementwise(std::false_type{});
-      }
+      for (int j = 0; j < 16; ++j) pacc[j] = sacc[j] * (pacc[j] - Dr[j / 4][j % 4]);
 
       // P^T and dS^T as A operands (row = key, k = query): k-slot i of 16-query
       // step s2 is query 16*s2 + 8*(i/4) + 4*h + i%4 of this wave's half.
@@ -309,6 +303,21 @@ void attn_bwd_dkdv_kernel(Args a) {
         const rsrc_t rS = make_rsrc(ds_head + (int64_t)qt * 2048, in_range ? 2048 : 0);
         buf_store128_nt(rS, c32 * 64 + h * 32, dsf[0]);
         buf_store128_nt(rS, c32 * 64 + h * 32 + 16, dsf[1]);
+      }
+    };
+    // Tiles crossing an edge of the band and the partial last key block are
+    // masked (zero-filled key rows would otherwise give P = exp(-LSE), which
+    // could overflow a 16-bit dS); every pair of an unmasked tile is
+    // visible: its lowest query sees its highest key and its highest query
+    // its lowest key.  One branch per tile, around the whole phase.
+    auto phase1 = [&](int m, int st) {
+      const bool masked = (BANDED && (kv0 + BN - 1 > m * BM + off_causal + a.win_r ||
+                                      kv0 < m * BM + BM - 1 + off_causal - a.win_l)) ||
+                          rows_k < BN;
+      if (masked) {
+        phase1_body(m, st, std::true_type{});
+      } else {
+        phase1_body(m, st, std::false_type{});
       }
     };
 
