@@ -47,7 +47,9 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(Args a) {
     acc += __shfl_xor(acc, 4);
     acc += __shfl_xor(acc, 8);
     if (sub == 0 && r < s.sq) {
-      a.delta[st0 + r] = acc;
+      // the workspace keeps -Delta: the gradient kernels start the dP
+      // accumulator from it, so dP - Delta costs no vector instruction
+      a.delta[st0 + r] = -acc;
       if (a.delta_out) a.delta_out[st0 + r] = acc;
     } else if (sub == 1 && r < s.sq) {
       // the exp2-domain LSE the dK/dV kernel stages with Delta

@@ -403,7 +403,7 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   };
   auto stageM = [&](f32x16& sv, f32x16& pv, u32x4* dsv, auto jc) {
     constexpr int j = decltype(jc)::value;
-    pv[j] = sv[j] * (pv[j] - Dl);
+    pv[j] = sv[j] * (pv[j] + Dl);  // Dl holds -Delta
     // dS as the A operand of dQ = dS K (row = query, k = key): k-slot e of
     // 16-key step s2 is key 16*s2 + 8*(e/4) + 4*h + e%4 of the half.
     if constexpr (j & 1) dsv[j >> 3][(j & 7) >> 1] = pack2<BF16>(pv[j - 1], pv[j]);

@@ -203,11 +203,18 @@ void attn_bwd_dkdv_kernel(Args a) {
       const float* sL = reinterpret_cast<const float*>(sQ + 2 * TILE);
       const float* sDl = sL + BM;
 
-      // LSE * log2(e) of this lane's 16 query rows (needed right after the S
-      // products); Delta is read under the dP products.
-      f32x4 Lr[4], Dr[4];
+      // LSE * log2(e) and -Delta of this lane's 16 query rows, in the order
+      // of the C layout's rows.  -Delta is the dP accumulator's start value,
+      // so the products leave dP - Delta.
+      f32x4 Lr[4];
+      f32x16 pacc;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) Lr[jj] = *reinterpret_cast<const f32x4*>(sL + 32 * half + 8 * jj + 4 * h);
+      for (int jj = 0; jj < 4; ++jj) {
+        Lr[jj] = *reinterpret_cast<const f32x4*>(sL + 32 * half + 8 * jj + 4 * h);
+        const f32x4 nd = *reinterpret_cast<const f32x4*>(sDl + 32 * half + 8 * jj + 4 * h);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pacc[4 * jj + r] = nd[r];
+      }
 
       // Visibility of the tile's (query, key) pairs (masked tiles only).
       // C layout of S / dP: lane = key column kv_lane, rows = queries
@@ -225,7 +232,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       // LSE2) runs on the vector ALU under the dP products.  The products go
       // out at raised priority: the other wave on this SIMD is in phase 2
       // (matrix-core work only) and fills the gaps.
-      f32x16 sacc = f32x16{}, pacc = f32x16{};
+      f32x16 sacc = f32x16{};
       {
         constexpr int NS = D / 16, PD = 3;
         static_assert(16 % NS == 0, "P elements spread evenly over the dP products");
@@ -257,10 +264,6 @@ void attn_bwd_dkdv_kernel(Args a) {
             sacc = mfma32<BF16>(op, kf[i], sacc);
           } else {
             pacc = mfma32<BF16>(op, vf[i - NS], pacc);
-            if (i == NS + 1) {
-#pragma unroll
-              for (int jj = 0; jj < 4; ++jj) Dr[jj] = *reinterpret_cast<const f32x4*>(sDl + 32 * half + 8 * jj + 4 * h);
-            }
             // 16 / NS elements of P per dP product
             constexpr int EPP = 16 / NS;
 #pragma unroll
@@ -273,7 +276,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       }
       // dS = P o (dP - Delta)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) pacc[j] = sacc[j] * (pacc[j] - Dr[j / 4][j % 4]);
+      for (int j = 0; j < 16; ++j) pacc[j] = sacc[j] * pacc[j];
 
       // P^T and dS^T as A operands (row = key, k = query): k-slot i of 16-query
       // step s2 is query 16*s2 + 8*(i/4) + 4*h + i%4 of this wave's half.
