@@ -48,7 +48,6 @@ attn_status validate_common(const attn_params* p) {
   if (p->heads_q <= 0 || p->heads_kv <= 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->heads_q % p->heads_kv) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->head_dim <= 0 || p->head_dim % 8 || p->head_dim > 256) return ATTN_ERR_INVALID_ARGUMENT;
-  if (p->head_dim > 128) return ATTN_ERR_UNSUPPORTED;
   if (p->seqlen_q < 0 || p->seqlen_k < 0) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->causal != 0 && p->causal != 1) return ATTN_ERR_INVALID_ARGUMENT;
   if (p->window_left < -1 || p->window_right < -1) return ATTN_ERR_INVALID_ARGUMENT;
@@ -113,7 +112,11 @@ size_t ds_bytes(const attn_params* p) {
 // a plain product over them).  Minimal workspace: the statistics only (the dQ
 // kernel then recomputes dS).
 size_t workspace_bytes(const attn_params* p) { return delta_bytes(p) + ds_bytes(p); }
-size_t workspace_bytes_min(const attn_params* p) { return delta_bytes(p); }
+// Head dims above 128 have only the stored-dS path: their minimum is the full
+// workspace.
+size_t workspace_bytes_min(const attn_params* p) {
+  return p->head_dim > 128 ? workspace_bytes(p) : delta_bytes(p);
+}
 
 Args make_args(const attn_params* p) {
   Args a;
@@ -171,18 +174,24 @@ template <bool BF16>
 void launch_fwd(const Args& a, int dtile, bool causal, dim3 grid, hipStream_t st) {
   if (dtile == 64)
     launch_fwd_d<BF16, 64>(a, causal, grid, st);
-  else
+  else if (dtile == 128)
     launch_fwd_d<BF16, 128>(a, causal, grid, st);
+  else
+    launch_fwd_d<BF16, 256>(a, causal, grid, st);
+}
+
+template <bool BF16, int D>
+void launch_dkdv_d(const Args& a, bool causal, dim3 grid_kv, hipStream_t st) {
+  const dim3 blk(64 * attn::dkdv_waves(D));
+  if (causal)
+    hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, true>), grid_kv, blk, 0, st, a);
+  else
+    hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, false>), grid_kv, blk, 0, st, a);
 }
 
 template <bool BF16, int D>
 void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q, hipStream_t st) {
-  if (phases & ATTN_PHASE_DKDV) {
-    if (causal)
-      hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, true>), grid_kv, dim3(512), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, false>), grid_kv, dim3(512), 0, st, a);
-  }
+  if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, D>(a, causal, grid_kv, st);
   if (phases & ATTN_PHASE_DQ) {
     const dim3 blk(64 * attn::kDqWaves);
     if (a.ds != nullptr) {  // dS^T written by the dK/dV kernel: plain product
@@ -199,16 +208,34 @@ void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, d
   }
 }
 
+int dtile_for(int head_dim) { return head_dim <= 64 ? 64 : (head_dim <= 128 ? 128 : 256); }
+
 template <bool BF16>
 void launch_grads(const Args& a, int dtile, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q,
                   hipStream_t st) {
-  if (dtile == 64)
+  if (dtile == 64) {
     launch_grads_d<BF16, 64>(a, causal, phases, grid_kv, grid_q, st);
-  else
+  } else if (dtile == 128) {
     launch_grads_d<BF16, 128>(a, causal, phases, grid_kv, grid_q, st);
+  } else {
+    // 256-wide tile: dK/dV in one kernel; dQ = dS K is column-separable, so
+    // the stored-dS product runs once per 128-wide half of the head dim (K
+    // and dQ offset by 128 elements, the second half's width the rest).
+    if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, 256>(a, causal, grid_kv, st);
+    if (phases & ATTN_PHASE_DQ) {
+      Args lo = a, hi = a;
+      lo.head_dim = 128;
+      hi.head_dim = a.head_dim - 128;
+      hi.k = a.k + 128;
+      hi.dq = a.dq + 128;
+      launch_grads_d<BF16, 128>(lo, causal, ATTN_PHASE_DQ, grid_kv, grid_q, st);
+      if (dtile_for(hi.head_dim) == 64)
+        launch_grads_d<BF16, 64>(hi, causal, ATTN_PHASE_DQ, grid_kv, grid_q, st);
+      else
+        launch_grads_d<BF16, 128>(hi, causal, ATTN_PHASE_DQ, grid_kv, grid_q, st);
+    }
+  }
 }
-
-int dtile_for(int head_dim) { return head_dim <= 64 ? 64 : 128; }
 
 }  // namespace
 
@@ -290,6 +317,8 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   // the stored-dS path addresses one head's dS tiles with 32-bit offsets
   const bool ds_fits = (int64_t)(4 * ((p->seqlen_k + 127) / 128) + 4) * ds_nqt(p) * 2048 < ((int64_t)1 << 30);
   const bool use_ds = ds_fits && workspace_bytes_given >= workspace_bytes(p);
+  // head dims above 128 have no recompute path for dQ
+  if (p->head_dim > 128 && !use_ds) return ds_fits ? ATTN_ERR_WORKSPACE_TOO_SMALL : ATTN_ERR_UNSUPPORTED;
 
   Args a = make_args(p);
   a.q = static_cast<const uint16_t*>(q);
@@ -324,7 +353,8 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
     if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
   }
   unsigned grad_phases = phases & (ATTN_PHASE_DKDV | ATTN_PHASE_DQ);
-  const int kvblocks = (p->seqlen_k + attn::kDkvBN - 1) / attn::kDkvBN;
+  const int kvbn = attn::dkdv_bn(dt);
+  const int kvblocks = (p->seqlen_k + kvbn - 1) / kvbn;
   const int dqblocks = (p->seqlen_q + attn::kDqBM - 1) / attn::kDqBM;
   if (kvblocks == 0) grad_phases &= ~ATTN_PHASE_DKDV;  // no keys: nothing to write in dK/dV
   if (dqblocks == 0) grad_phases &= ~ATTN_PHASE_DQ;    // no queries: no dQ rows

@@ -29,7 +29,11 @@
 namespace attn {
 
 constexpr int kDkvBM = 64;    // query rows per iteration of the dK/dV kernel
-constexpr int kDkvBN = 128;   // key rows per dK/dV workgroup
+// Key rows per dK/dV workgroup: 16 per wave.  Head dims up to 128 run 8 waves
+// (two per SIMD, 128 keys); the 256-wide tile runs 4 waves (one per SIMD,
+// 64 keys), whose K, V and accumulators take twice the registers.
+constexpr int dkdv_waves(int d) { return d > 128 ? 4 : 8; }
+constexpr int dkdv_bn(int d) { return 16 * dkdv_waves(d); }
 
 // ---------------------------------------------------------------------------
 // dK / dV: one workgroup per (128-key block, KV head, sequence), looping over
@@ -43,21 +47,25 @@ constexpr int kDkvBN = 128;   // key rows per dK/dV workgroup
 // exchange (8 x 4 KiB).
 // ---------------------------------------------------------------------------
 template <bool BF16, int D, bool BANDED>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * dkdv_waves(D)) __attribute__((amdgpu_waves_per_eu(dkdv_waves(D) / 4, dkdv_waves(D) / 4)))
 void attn_bwd_dkdv_kernel(Args a) {
-  constexpr int BM = kDkvBM, BN = kDkvBN;
+  constexpr int NW = dkdv_waves(D);
+  constexpr int BM = kDkvBM, BN = dkdv_bn(D);
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RB = D * 2;                  // bytes per row
   constexpr int TILE = BM * RB;
   constexpr int STAGE = 2 * TILE + 2 * BM * 4;
   constexpr int TD = D / 32;                 // head-dim tiles
   constexpr int TDH = TD / 2;                // head-dim tiles per half
-  constexpr int QI = BM * CPR / 512;         // direct loads per wave per Q (or dO) tile
+  constexpr int QI = BM * CPR / (64 * NW);   // direct loads per wave per Q (or dO) tile
   constexpr int NPF = 2 * QI + 1;            // direct loads per wave per tile (Q, dO, one stat row)
-  constexpr int NSTAGE = 3;
+  // stages of {Q, dO, LSE, Delta}: three (loads two tiles ahead) when they
+  // fit in LDS, else two (one tile ahead)
+  constexpr int NSTAGE = NW == 8 ? 3 : 2;
   constexpr int XB = 4 * 16 * 64;            // exchange bytes per wave
-  constexpr int SINK = NSTAGE * STAGE + 8 * XB;  // 256 bytes the idle waves' stat loads land in
-  static_assert(TDH >= 1 && QI >= 1, "head dim of 64 or 128");
+  constexpr int SINK = NSTAGE * STAGE + NW * XB;  // 256 bytes the idle waves' stat loads land in
+  static_assert(TDH >= 1 && QI >= 1, "head dim tile of 64, 128 or 256");
+  static_assert(SINK + 256 <= 160 * 1024, "LDS");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SINK + 256];
   const uint32_t smem_lds = lds_addr(smem);
@@ -134,12 +142,12 @@ void attn_bwd_dkdv_kernel(Args a) {
   int qdma[QI], dodma[QI];
 #pragma unroll
   for (int i = 0; i < QI; ++i) {
-    const int S = (i * 8 + w) * 64 + lane;
+    const int S = (i * NW + w) * 64 + lane;
     qdma[i] = slot_off(S, (int)a.q_r);
     dodma[i] = slot_off(S, (int)a.do_r);
   }
 
-  const int64_t ds_slot = ds_key_slot0(a, z) + 4 * nb + kvg;  // this wave's 32-key tile in dS^T
+  const int64_t ds_slot = ds_key_slot0(a, z) + (BN / 32) * nb + kvg;  // this wave's 32-key tile in dS^T
   // query tiles that see any key of this block
   int m_begin = 0, m_end = (s.sq + BM - 1) / BM;
   if (BANDED) {
@@ -184,7 +192,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       const uint32_t to = real ? (uint32_t)(m * BM) * (uint32_t)a.do_r * 2u : (uint32_t)kOffOOB;
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
-        const int S0 = (i * 8 + w) * 64;
+        const int S0 = (i * NW + w) * 64;
         dma16(srdQh, (int)((uint32_t)qdma[i] + tq), stage + S0 * 16);
         dma16(srdOh, (int)((uint32_t)dodma[i] + to), stage + TILE + S0 * 16);
       }
@@ -362,55 +370,77 @@ void attn_bwd_dkdv_kernel(Args a) {
       }
     };
 
-    // Two groups of four waves (two pairs each) run half a tile apart: in
-    // every interval between barriers one wave of each SIMD is in phase 1
-    // (products, then the softmax on the vector ALU) and the other in phase
-    // 2 (products only), so the softmax of one overlaps the other's matrix
-    // work.  Both groups run the same straight loop body, phase 1, barrier,
-    // phase 2, barrier; group 1 enters it one barrier late (s_barrier counts
-    // arrivals, not program locations) and group 0 passes one extra barrier
-    // at the end, so interval k holds group 0's phase (k & 1) of tile k / 2
-    // and group 1's phase ((k - 1) & 1) of tile (k - 1) / 2.
-    // Tile j (relative) lives in stage j % 3.  Tile j + 2 is loaded at the
-    // start of interval 2j + 1 (group 0's phase 2 of tile j, group 1's phase
-    // 1), after the barrier that ends the last read of its stage (group 1's
-    // phase 2 of tile j - 1), and this wave's share of tile j + 1 is waited
-    // for at the end of interval 2j + 1, before group 0 reads it.
-    //
-    // Memory-counter accounting: after tile j + 1's loads a group-0 wave
-    // issues two dS^T stores (phase 1 of tile j) and tile j + 2's loads; a
-    // group-1 wave issues the stores of tile j - 1, tile j + 2's loads and the
-    // stores of tile j.  Two empty stores stand in for tile -1's.
-    const int n = m_end - m_begin;
-    // The previous head's last interval ended with a barrier: every wave is
-    // done with its stages.
-    prefetch(m_begin, 0, true);
-    prefetch(m_begin + 1, 1, n > 1);
-    if (grp) {
-      const rsrc_t none = make_rsrc(a.q, 0);
-      buf_store128_nt(none, 0, u32x4{0u, 0u, 0u, 0u});
-      buf_store128_nt(none, 16, u32x4{0u, 0u, 0u, 0u});
-      wait_vmcnt<NPF + 2>();
-    } else {
-      wait_vmcnt<NPF>();
+    if constexpr (NSTAGE == 3) {
+      // Two groups of four waves (two pairs each) run half a tile apart: in
+      // every interval between barriers one wave of each SIMD is in phase 1
+      // (products, then the softmax on the vector ALU) and the other in phase
+      // 2 (products only), so the softmax of one overlaps the other's matrix
+      // work.  Both groups run the same straight loop body, phase 1, barrier,
+      // phase 2, barrier; group 1 enters it one barrier late (s_barrier counts
+      // arrivals, not program locations) and group 0 passes one extra barrier
+      // at the end, so interval k holds group 0's phase (k & 1) of tile k / 2
+      // and group 1's phase ((k - 1) & 1) of tile (k - 1) / 2.
+      // Tile j (relative) lives in stage j % 3.  Tile j + 2 is loaded at the
+      // start of interval 2j + 1 (group 0's phase 2 of tile j, group 1's phase
+      // 1), after the barrier that ends the last read of its stage (group 1's
+      // phase 2 of tile j - 1), and this wave's share of tile j + 1 is waited
+      // for at the end of interval 2j + 1, before group 0 reads it.
+      //
+      // Memory-counter accounting: after tile j + 1's loads a group-0 wave
+      // issues two dS^T stores (phase 1 of tile j) and tile j + 2's loads; a
+      // group-1 wave issues the stores of tile j - 1, tile j + 2's loads and the
+      // stores of tile j.  Two empty stores stand in for tile -1's.
+      const int n = m_end - m_begin;
+      // The previous head's last interval ended with a barrier: every wave is
+      // done with its stages.
+      prefetch(m_begin, 0, true);
+      prefetch(m_begin + 1, 1, n > 1);
+      if (grp) {
+        const rsrc_t none = make_rsrc(a.q, 0);
+        buf_store128_nt(none, 0, u32x4{0u, 0u, 0u, 0u});
+        buf_store128_nt(none, 16, u32x4{0u, 0u, 0u, 0u});
+        wait_vmcnt<NPF + 2>();
+      } else {
+        wait_vmcnt<NPF>();
+      }
+      lds_barrier();  // tile 0 landed
+      if (grp) lds_barrier();  // interval 0: group 0's phase 1 of tile 0
+      int st = 0, st_load = 2;
+      for (int j = 0; j < n; ++j) {
+        if (grp) prefetch(m_begin + j + 2, st_load, j + 2 < n);
+        phase1(m_begin + j, st);
+        if (grp) wait_vmcnt<NPF + 4>();
+        lds_barrier();  // exchange slots written
+        if (!grp) prefetch(m_begin + j + 2, st_load, j + 2 < n);
+        phase2(st);
+        if (!grp) wait_vmcnt<NPF + 2>();
+        lds_barrier();  // loads published; stage reads retired
+        st = st == 2 ? 0 : st + 1;
+        st_load = st_load == 2 ? 0 : st_load + 1;
+      }
+      if (!grp) lds_barrier();  // interval 2n: group 1's phase 2 of the last tile
+      } else {
+      // One wave per SIMD, one group: phase 1, barrier, phase 2, barrier per
+      // tile.  Tile j + 1 is loaded into the other stage at the start of
+      // tile j (its stage was last read in phase 2 of tile j - 1) and waited
+      // for at the end of tile j; after its loads a wave issues only tile j's
+      // two dS^T stores.
+      const int n = m_end - m_begin;
+      prefetch(m_begin, 0, true);
+      wait_vmcnt<0>();
+      lds_barrier();  // tile 0 landed
+      int st = 0;
+      for (int j = 0; j < n; ++j) {
+        prefetch(m_begin + j + 1, st ^ 1, j + 1 < n);
+        phase1(m_begin + j, st);
+        lds_barrier();  // exchange slots written
+        phase2(st);
+        wait_vmcnt<2>();
+        lds_barrier();  // loads published; stage reads retired
+        st ^= 1;
+      }
     }
-    lds_barrier();  // tile 0 landed
-    if (grp) lds_barrier();  // interval 0: group 0's phase 1 of tile 0
-    int st = 0, st_load = 2;
-    for (int j = 0; j < n; ++j) {
-      if (grp) prefetch(m_begin + j + 2, st_load, j + 2 < n);
-      phase1(m_begin + j, st);
-      if (grp) wait_vmcnt<NPF + 4>();
-      lds_barrier();  // exchange slots written
-      if (!grp) prefetch(m_begin + j + 2, st_load, j + 2 < n);
-      phase2(st);
-      if (!grp) wait_vmcnt<NPF + 2>();
-      lds_barrier();  // loads published; stage reads retired
-      st = st == 2 ? 0 : st + 1;
-      st_load = st_load == 2 ? 0 : st_load + 1;
-    }
-    if (!grp) lds_barrier();  // interval 2n: group 1's phase 2 of the last tile
-  }
+}
 
   // ---- Epilogue: dK * scale, dV; convert (round to nearest even) and store.
   const uint16_t* dkb = a.dk + s.bk * a.dk_b + (int64_t)(s.k0 + kv0) * a.dk_r + (int64_t)g * a.dk_h;

@@ -403,8 +403,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // ---------------------------------------------------------------------------
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
-  static_assert(CPR == 8 || CPR == 16, "rows of 128 or 256 bytes");
-  if constexpr (CPR == 16) {
+  static_assert(CPR == 8 || CPR == 16 || CPR == 32, "rows of 128, 256 or 512 bytes");
+  // 512-byte rows cover the 64 banks twice: permuting the low four chunk
+  // bits as for 256-byte rows gives every access pattern the same bank
+  // spread (bank group = chunk mod 16).
+  if constexpr (CPR == 16 || CPR == 32) {
     return 4 * (r & 3) + ((r >> 2) & 3);
   } else {
     return 4 * ((r >> 1) & 1) + ((r >> 2) & 3);

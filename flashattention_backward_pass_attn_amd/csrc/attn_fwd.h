@@ -26,8 +26,13 @@ namespace attn {
 constexpr int kFwdBM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kFwdBN = 64;   // key rows per iteration
 
+// Head dims up to 128 run two waves per SIMD; the 256-wide tile (Q, the
+// O accumulator and the next K/V block all in registers) runs one.
+constexpr int fwd_waves_per_simd(int d) { return d > 128 ? 1 : 2; }
+
 template <bool BF16, int D, bool BANDED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(D), fwd_waves_per_simd(D))))
+void attn_fwd_kernel(Args a) {
   constexpr int BM = kFwdBM, BN = kFwdBN, LD = D + 8;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int NCH = BN * CPR / 256;     // chunks per thread per K (or V) block

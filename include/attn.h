@@ -65,10 +65,9 @@ typedef struct {
   int32_t seqlen_k;        /* fixed-length Sk (>= 0); varlen: max length */
   int32_t heads_q;         /* H > 0 */
   int32_t heads_kv;        /* Hk > 0, H % Hk == 0 */
-  int32_t head_dim;        /* d % 8 == 0, d <= 256; d <= 128 is built (each
-                              head is computed in a 64- or 128-wide tile,
-                              zero-padded); 136..256 gives
-                              ATTN_ERR_UNSUPPORTED */
+  int32_t head_dim;        /* d % 8 == 0, d <= 256 (the CK mha_bwd.cpp
+                              page's limit); each head is computed in a 64-,
+                              128- or 256-wide tile, zero-padded */
   float softmax_scale;     /* scores are scale * Q K^T, scale > 0 (finite);
                               pass 1/sqrt(d) for the default */
   int32_t causal;          /* 0/1; key j visible to query i iff
@@ -93,7 +92,6 @@ typedef struct {
 /*
  * Limits of this build, reported as ATTN_ERR_UNSUPPORTED before any launch
  * (the arguments are valid for the method):
- *   head_dim above 128;
  *   heads_q or batch above 65535, or heads_q * batch above 2^31 - 1;
  *   seqlen_q or seqlen_k above 65535 * 64;
  *   a per-head extent of 1 GiB or more: seqlen * row stride * 2 bytes, for
@@ -128,13 +126,15 @@ attn_status attn_fwd(const attn_params *p, const void *q, const void *k, const v
  * the dK/dV kernel, which forms dS anyway, stores it and the dQ kernel is a
  * plain product dQ = scale * dS K over it.  (When one head's dS tiles
  * would span 1 GiB or more -- sequences of roughly 23K keys and up -- the
- * recompute path below is used whatever the workspace.)  Never allocates.
+ * recompute path below is used whatever the workspace; for head_dim above
+ * 128, which has no recompute path, attn_bwd then returns
+ * ATTN_ERR_UNSUPPORTED.)  Never allocates.
  */
 attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
 
 /*
  * Bytes of the smallest workspace attn_bwd accepts: the two row statistics
- * only.  With a
+ * only (for head_dim above 128: the full workspace, as above).  With a
  * workspace smaller than attn_bwd_workspace_size() (but at least this), the
  * dQ kernel recomputes S, dP and dS per key tile instead of reading them:
  * more arithmetic, no quadratic memory.  Results are identical in value up

@@ -81,7 +81,6 @@ def _fwd(clib, p, ptr=FAKE):
     ("batch", 0, fa.ATTN_ERR_INVALID_ARGUMENT),
     ("head_dim", 60, fa.ATTN_ERR_INVALID_ARGUMENT),       # not a multiple of 8
     ("head_dim", 264, fa.ATTN_ERR_INVALID_ARGUMENT),      # above 256
-    ("head_dim", 192, fa.ATTN_ERR_UNSUPPORTED),           # valid, not built
     ("heads_kv", 3, fa.ATTN_ERR_INVALID_ARGUMENT),        # 8 % 3 != 0
     ("seqlen_q", -1, fa.ATTN_ERR_INVALID_ARGUMENT),
     ("causal", 2, fa.ATTN_ERR_INVALID_ARGUMENT),
@@ -153,3 +152,17 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 8, 2, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa.attn_fwd(q, q, q)
+
+
+def test_wide_head_dim_needs_the_full_workspace(clib):
+    """Head dims above 128 (the 256-wide tile) have only the stored-dS path: the
+    minimum workspace is the full one, and a Delta-only workspace is refused
+    before anything is launched."""
+    for d in (136, 192, 256):
+        p = _params(head_dim=d)
+        n = ctypes.c_size_t(0)
+        nmin = ctypes.c_size_t(0)
+        assert clib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == fa.ATTN_OK
+        assert clib.attn_bwd_workspace_size_min(ctypes.byref(p), ctypes.byref(nmin)) == fa.ATTN_OK
+        assert nmin.value == n.value
+        assert _bwd(clib, p, ws_bytes=n.value - 256) == fa.ATTN_ERR_WORKSPACE_TOO_SMALL

@@ -76,6 +76,41 @@ def test_small_parity_minimal_workspace(lib, case):
     _compare(out, ref, case[1])
 
 
+# Head dims above 128 run the 256-wide tile (dK/dV in one kernel, dQ as two
+# 128-wide halves of the stored-dS product); same layout as SMALL_CASES.
+WIDE_CASES = [
+    ("d256_bf16_causal_ragged", "bf16", 2, 4, 2, 200, 200, 256, True, None),
+    ("d192_fp16_noncausal_gqa", "fp16", 1, 8, 2, 257, 190, 192, False, None),
+    ("d256_fp16_causal_sq_lt_sk", "fp16", 1, 2, 1, 77, 301, 256, True, None),
+    ("d192_bf16_varlen_causal", "bf16", 4, 4, 2, 0, 0, 192, True, ([1, 130, 257, 64], [1, 130, 257, 64])),
+    ("d136_fp16_causal", "fp16", 1, 2, 2, 150, 150, 136, True, None),
+    ("d256_bf16_noncausal_s1", "bf16", 1, 2, 2, 1, 1, 256, False, None),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=[c[0] for c in WIDE_CASES])
+def test_wide_head_dim_parity(lib, case):
+    print(f"[gpu] wide head dim parity {case[0]}", flush=True)
+    inp = _inputs(case, seed=777)
+    causal = case[8]
+    out = gpu_run(lib, inp, causal)
+    ref = oracle_run(inp, causal)
+    _compare(out, ref, case[1])
+
+
+def test_wide_head_dim_window_and_determinism(lib):
+    """A local window at d = 256, and bit-identical gradients from run to run."""
+    print("[gpu] wide head dim window + determinism d256 bf16", flush=True)
+    case = ("d256_window", "bf16", 1, 2, 2, 300, 300, 256, False, None)
+    inp = _inputs(case, seed=778)
+    a = gpu_run(lib, inp, False, window=(100, 20))
+    b = gpu_run(lib, inp, False, window=(100, 20))
+    ref = oracle_run(inp, False, window=(100, 20))
+    _compare(a, ref, "bf16")
+    for name in ("dq", "dk", "dv"):
+        assert np.array_equal(_bits(a[name]), _bits(b[name])), name
+
+
 # local (sliding-window) attention: name, dtype, b, h, hk, sq, sk, d, causal, lens, (left, right)
 WINDOW_CASES = [
     ("window_fp16_l100_r30_d64", "fp16", 1, 2, 2, 300, 300, 64, False, None, (100, 30)),
