@@ -184,7 +184,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default=workloads.DEFAULT_BENCH_WORKLOAD, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", default=workloads.DEFAULT_BENCH_WORKLOAD, choices=sorted(workloads.ALL_WORKLOADS))
     ap.add_argument("--deterministic", action="store_true")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
                     help="CPU time budget of the oracle sample (0 disables the cpu_baseline leg)")
@@ -210,7 +210,7 @@ def main(argv=None):
 
     import flashattention_backward_pass_attn_amd as fa
 
-    w = workloads.WORKLOADS[args.workload]
+    w = workloads.ALL_WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     inp = workloads.make_workload_inputs(w.name)

@@ -28,6 +28,8 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "DEFAULT_BENCH_WORKLOAD",
+    "BENCH_EXTRA",
+    "ALL_WORKLOADS",
     "PARITY_SMALL_WORKLOAD",
     "round_bf16_bits",
     "bf16_bits_to_f32",
@@ -73,6 +75,19 @@ WORKLOADS = {
                  varlen_range=(256, 4096), note="packed sequences, causal per sequence"),
     ]
 }
+# Measurement-only shapes for bench.py --workload (not parity configs): the
+# timed workload in fp16 (the fp16/bf16 matrix peaks are equal), and the
+# 256-wide head-dim tile.  Seeds continue after the five above.
+BENCH_EXTRA = {
+    w.name: w
+    for w in [
+        Workload("mha_causal_fp16_b4_h16_s4096_d128", "fp16", 4, 16, 16, 4096, 128, True, 47,
+                 do_scale=0.1, note="the timed workload in fp16"),
+        Workload("mha_causal_bf16_b2_h16_s4096_d256", "bf16", 2, 16, 16, 4096, 256, True, 48,
+                 do_scale=0.1, note="head dim 256"),
+    ]
+}
+ALL_WORKLOADS = {**WORKLOADS, **BENCH_EXTRA}
 DEFAULT_BENCH_WORKLOAD = "mha_causal_bf16_b4_h16_s4096_d128"
 PARITY_SMALL_WORKLOAD = "mha_fp16_b1_h2_s128_d64"
 
@@ -159,7 +174,7 @@ def make_inputs(
 
 
 def make_workload_inputs(name: str, seed: Optional[int] = None):
-    w = WORKLOADS[name]
+    w = ALL_WORKLOADS[name]
     return make_inputs(
         w.dtype, w.batch, w.heads_q, w.heads_kv, w.seqlen, w.seqlen, w.head_dim,
         w.seed if seed is None else seed, do_scale=w.do_scale, varlen_range=w.varlen_range,
