@@ -25,6 +25,10 @@ namespace attn {
 
 constexpr int kFwdBM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int kFwdBN = 64;   // key rows per iteration
+// The running row maximum (log2 units) is moved only when a row grows past it
+// by more than this, so P <= 2^8 = 256: exact in fp32 sums, and within the
+// fp16 and bf16 range of the P operand.
+constexpr float kFwdRescaleSlack = 8.f;
 
 // Head dims up to 128 run two waves per SIMD; the 256-wide tile (Q, the
 // O accumulator and the next K/V block all in registers) runs one.
@@ -155,9 +159,21 @@ void attn_fwd_kernel(Args a) {
       for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[tk][j]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    // Lazy rescaling: the exponent reference m_run moves only when some row
+    // of the wave grew by more than kFwdRescaleSlack (log2 units); otherwise
+    // P may exceed 1 by up to 2^kFwdRescaleSlack, O and the row sum keep
+    // their scale, and the multiply of the O accumulator is skipped.  O / l
+    // and the LSE m_run + log2(l) are the same with either reference.
+    const bool rescale = __builtin_amdgcn_ballot_w64(mx > m_run + kFwdRescaleSlack) != 0;
+    float m_use, alpha = 1.f;
+    if (rescale) {
+      const float m_new = fmaxf(m_run, mx);
+      m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+    } else {
+      m_use = (m_run == -INFINITY) ? 0.f : m_run;
+    }
     float ls = 0.f;
 #pragma unroll
     for (int tk = 0; tk < TK; ++tk) {
@@ -170,9 +186,10 @@ void attn_fwd_kernel(Args a) {
     }
     ls += __shfl_xor(ls, 32);
     l_run = l_run * alpha + ls;
-    m_run = m_new;
+    if (rescale) {
 #pragma unroll
-    for (int t = 0; t < TD; ++t) oacc[t] *= alpha;
+      for (int t = 0; t < TD; ++t) oacc[t] *= alpha;
+    }
 
     // O^T += V^T P^T: P^T leaves the MFMA in B-operand layout (k = keys).
 #pragma unroll
