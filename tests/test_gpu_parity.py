@@ -172,7 +172,7 @@ def test_workload_mha_fp16_b1_h2_s128_d64(lib):
     """Forward + backward at the full size of the small non-causal workload."""
     name = "mha_fp16_b1_h2_s128_d64"
     print(f"[gpu] workload {name}", flush=True)
-    w = workloads.WORKLOADS[name]
+    w = workloads.ALL_WORKLOADS[name]
     inp = workloads.make_workload_inputs(name)
     out = gpu_run(lib, inp, w.causal)
     ref = oracle_run(inp, w.causal)
@@ -201,7 +201,7 @@ def test_workload_mha_causal_fp16_b2_h8_s1024_d64_atomic_and_deterministic(lib):
 def _full_size_sampled(lib, name, samples):
     """Run the whole workload on the GPU; compare sampled (sequence, KV head) slices to the oracle."""
     import oracle
-    w = workloads.WORKLOADS[name]
+    w = workloads.ALL_WORKLOADS[name]
     inp = workloads.make_workload_inputs(name)
     out = gpu_run(lib, inp, w.causal)
     scale = 1.0 / math.sqrt(w.head_dim)
@@ -251,6 +251,18 @@ def _sum_checks(dk, dv, do, G):
     assert np.abs(s_dk).max() <= 1e-2 * np.abs(dk).sum(axis=1).max() + 1e-6
     want = do.sum(axis=1).reshape(b, hk, G, d).sum(axis=2)
     assert np.abs(dv.sum(axis=1) - want).max() <= 2e-2 * max(np.abs(want).max(), 1e-6)
+
+
+def test_measured_shape_causal_bf16_b2_h16_s4096_d256_sampled(lib):
+    """The head-dim-256 shape bench.py measures, at full size in its launch
+    configuration: sampled heads against the oracle plus the sum properties."""
+    print("[gpu] full-size causal bf16 B2 H16 S4096 d256 (sampled heads)", flush=True)
+    _full_size_sampled(lib, "mha_causal_bf16_b2_h16_s4096_d256", [(0, 0), (1, 15)])
+
+
+def test_measured_shape_causal_fp16_b4_h16_s4096_d128_sampled(lib):
+    print("[gpu] full-size causal fp16 B4 H16 S4096 d128 (sampled heads)", flush=True)
+    _full_size_sampled(lib, "mha_causal_fp16_b4_h16_s4096_d128", [(2, 7)])
 
 
 def test_workload_mha_causal_bf16_b4_h16_s4096_d128_sampled(lib):
