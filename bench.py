@@ -36,6 +36,11 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 MFMA_PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
+# What flashattention_backward_pass_attn_amd/csrc/mfma_peak.hip sustains on an
+# MI355X with nothing but 32x32x16 products in flight (clock about 1.93 GHz
+# under that load); profiles/mfma_rate_and_valu_overlap_mi355x.md.  Context
+# for the roofline fraction, not its denominator.
+MFMA_MEASURED_TFLOPS = {"fp16": 1905.1, "bf16": 2026.2}
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_backward_pass_attn_amd/csrc/attn_bwd_split.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_bwd_dq.h",
@@ -304,6 +309,8 @@ def main(argv=None):
         "kernel_ms": per_kernel[dom]["ms"],
         "kernels": per_kernel,
         "preprocess_ms": round(pre_ms, 4),
+        "measured_peak": MFMA_MEASURED_TFLOPS[w.dtype],
+        "frac_of_measured_peak": round(per_kernel[dom]["tflops"] / MFMA_MEASURED_TFLOPS[w.dtype], 4),
     }
     cpu = None
     if args.cpu_baseline_seconds > 0:
