@@ -15,8 +15,10 @@
 // probabilities P^T leave the MFMA already in the operand layout of
 // O^T += V^T P^T.  V^T is read from the row-major V tile in LDS with the LDS
 // transpose read, so no transposed copy is written.  Q stays in registers for
-// the whole kernel; the next K/V block is prefetched into registers while the
-// current one is used.
+// the whole kernel; K/V blocks come straight from global memory into two LDS
+// stages (direct global->LDS loads, one block ahead), laid out with the
+// 16-byte-chunk swizzle that keeps both the row reads of K and the transposed
+// reads of V free of bank conflicts.
 #pragma once
 
 #include "attn_device.h"
@@ -30,22 +32,25 @@ constexpr int kFwdBN = 64;   // key rows per iteration
 // fp16 and bf16 range of the P operand.
 constexpr float kFwdRescaleSlack = 8.f;
 
-// Head dims up to 128 run two waves per SIMD; the 256-wide tile (Q, the
-// O accumulator and the next K/V block all in registers) runs one.
+// Head dims up to 128 run two waves per SIMD; the 256-wide tile (Q and the
+// O accumulator in registers) runs one.
 constexpr int fwd_waves_per_simd(int d) { return d > 128 ? 1 : 2; }
 
 template <bool BF16, int D, bool BANDED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(D), fwd_waves_per_simd(D))))
 void attn_fwd_kernel(Args a) {
-  constexpr int BM = kFwdBM, BN = kFwdBN, LD = D + 8;
+  constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
-  constexpr int NCH = BN * CPR / 256;     // chunks per thread per K (or V) block
+  constexpr int RB = D * 2;               // bytes per row
+  constexpr int TILE = BN * RB;           // one K (or V) block
+  constexpr int STAGE = 2 * TILE;         // K then V
+  constexpr int NCH = BN * CPR / 256;     // direct loads per thread per K (or V) block
   constexpr int TK = BN / 32;             // key tiles per block
   constexpr int TD = D / 32;              // head-dim tiles
   static_assert(BN * CPR % 256 == 0, "tile/thread mismatch");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * LD];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  const uint32_t smem_lds = lds_addr(smem);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -90,48 +95,72 @@ void attn_fwd_kernel(Args a) {
 
   const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
   const uint16_t* vbase = a.v + s.bk * a.v_b + (int64_t)s.k0 * a.v_r + (int64_t)g * a.v_h;
-
-  u32x4 kreg[NCH], vreg[NCH];
-  auto load_kv = [&](int nb) {
+  // One descriptor per tensor over the head's rows; a block is a 32-bit lane
+  // offset into it.  Rows past the end and columns past head_dim read as 0.
+  const u32x4 srdK = make_srd(kbase, ((int64_t)(s.sk - 1) * a.k_r + hd) * 2);
+  const u32x4 srdV = make_srd(vbase, ((int64_t)(s.sk - 1) * a.v_r + hd) * 2);
+  // 16-byte slot S of a block's LDS image holds row S / CPR, chunk
+  // (S % CPR) ^ swz(row).
+  int kdma[NCH], vdma[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int S = (i * 4 + w) * 64 + lane;
+    const int r = S / CPR;
+    const int c = (S % CPR) ^ swz<CPR>(r);
+    kdma[i] = 8 * c < hd ? (r * (int)a.k_r + 8 * c) * 2 : kOffOOB;
+    vdma[i] = 8 * c < hd ? (r * (int)a.v_r + 8 * c) * 2 : kOffOOB;
+  }
+  auto prefetch = [&](int nb, int st) {
+    const uint32_t stage = smem_lds + st * STAGE;
+    const uint32_t tk = (uint32_t)(nb * BN) * (uint32_t)a.k_r * 2u;
+    const uint32_t tv = (uint32_t)(nb * BN) * (uint32_t)a.v_r * 2u;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int id = tid + 256 * i;
-      const int r = id / CPR, c = id % CPR;
-      const int row = nb * BN + r;
-      const bool ok = row < s.sk && 8 * c < hd;
-      kreg[i] = ok ? ldg128(kbase + (int64_t)row * a.k_r + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-      vreg[i] = ok ? ldg128(vbase + (int64_t)row * a.v_r + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+      const uint32_t dst = stage + (uint32_t)((i * 4 + w) * 64) * 16u;
+      dma16(srdK, kdma[i] == kOffOOB ? kOffOOB : (int)((uint32_t)kdma[i] + tk), dst);
+      dma16(srdV, vdma[i] == kOffOOB ? kOffOOB : (int)((uint32_t)vdma[i] + tv), dst + TILE);
     }
   };
+  // K rows as the A operand of S^T (row = key c32 of a 32-key tile, k = head
+  // dim 16*sd + 8*h): step sd is at kvb ^ 32*sd (the swizzle permutes chunk
+  // bits only).  V^T for O^T += V^T P^T with the transposed read: key rows
+  // 4*h + rr (+8) of a 16-key step, head-dim columns 32*t + tcol.
+  const int sl = lane & 15;
+  const int kvb = tile_off<CPR>(c32, 8 * h);
+  const int rr = sl >> 2;
+  const int tcol = 16 * ((lane >> 4) & 1) + 4 * (sl & 3);
+  int va[TD], vb[TD];
+#pragma unroll
+  for (int t = 0; t < TD; ++t) {
+    va[t] = tile_off<CPR>(4 * h + rr, 32 * t + tcol);
+    vb[t] = tile_off<CPR>(4 * h + rr + 8, 32 * t + tcol);
+  }
 
   f32x16 oacc[TD];
 #pragma unroll
   for (int t = 0; t < TD; ++t) oacc[t] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const int tr_off = tr_lane_offset(lane, LD);
 
-  if (n_begin < n_end) load_kv(n_begin);
+  if (n_begin < n_end) {
+    prefetch(n_begin, 0);
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+  int st = 0;
   for (int nb = n_begin; nb < n_end; ++nb) {
-    __syncthreads();  // all waves are done with the previous block
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int id = tid + 256 * i;
-      const int r = id / CPR, c = id % CPR;
-      sts128(sK + r * LD + 8 * c, kreg[i]);
-      sts128(sV + r * LD + 8 * c, vreg[i]);
-    }
-    __syncthreads();
-    if (nb + 1 < n_end) load_kv(nb + 1);
+    // the other stage was last read in the previous block (barrier below)
+    if (nb + 1 < n_end) prefetch(nb + 1, st ^ 1);
+    const int sbase = st * STAGE;
 
     // S^T (keys x queries) for this lane's 32 query columns.
-    f32x16 st[TK];
+    f32x16 sc[TK];
 #pragma unroll
     for (int tk = 0; tk < TK; ++tk) {
-      st[tk] = f32x16{};
+      sc[tk] = f32x16{};
 #pragma unroll
       for (int sd = 0; sd < D / 16; ++sd) {
-        const u32x4 af = lds128(sK + (32 * tk + c32) * LD + 16 * sd + 8 * h);
-        st[tk] = mfma32<BF16>(af, qf[sd], st[tk]);
+        const u32x4 af = lds_rd128(smem, (sbase + 32 * tk * RB + kvb) ^ (32 * sd));
+        sc[tk] = mfma32<BF16>(af, qf[sd], sc[tk]);
       }
     }
 
@@ -148,7 +177,7 @@ void attn_fwd_kernel(Args a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int ks = nb * BN + 32 * tk + 8 * (j >> 2) + (j & 3);  // key minus the lane's 4*h
-          st[tk][j] = (ks <= kv_hi && ks >= kv_lo) ? st[tk][j] : -INFINITY;
+          sc[tk][j] = (ks <= kv_hi && ks >= kv_lo) ? sc[tk][j] : -INFINITY;
         }
       }
     }
@@ -156,7 +185,7 @@ void attn_fwd_kernel(Args a) {
 #pragma unroll
     for (int tk = 0; tk < TK; ++tk) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, st[tk][j]);
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[tk][j]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
     // Lazy rescaling: the exponent reference m_run moves only when some row
@@ -179,8 +208,8 @@ void attn_fwd_kernel(Args a) {
     for (int tk = 0; tk < TK; ++tk) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(__builtin_fmaf(st[tk][j], a.scale_log2, -m_use));
-        st[tk][j] = p;
+        const float p = fast_exp2(__builtin_fmaf(sc[tk][j], a.scale_log2, -m_use));
+        sc[tk][j] = p;
         ls += p;
       }
     }
@@ -198,15 +227,18 @@ void attn_fwd_kernel(Args a) {
       for (int s2 = 0; s2 < 2; ++s2) {
         u32x4 pf;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pf[e] = pack2<BF16>(st[tk][8 * s2 + 2 * e], st[tk][8 * s2 + 2 * e + 1]);
-        const int ra = 32 * tk + 16 * s2 + 4 * h;
+        for (int e = 0; e < 4; ++e) pf[e] = pack2<BF16>(sc[tk][8 * s2 + 2 * e], sc[tk][8 * s2 + 2 * e + 1]);
+        const int ro = sbase + TILE + (32 * tk + 16 * s2) * RB;
 #pragma unroll
         for (int t = 0; t < TD; ++t) {
-          const u32x4 vf = tr_frag(sV + 32 * t + tr_off, LD, ra, ra + 8);
+          const u32x4 vf = tr_frag_b(smem, ro + va[t], ro + vb[t]);
           oacc[t] = mfma32<BF16>(vf, pf, oacc[t]);
         }
       }
     }
+    wait_vmcnt<0>();  // block nb + 1 landed (this wave's share)
+    lds_barrier();    // everyone's share; every wave is done with stage st
+    st ^= 1;
   }
 
   // Normalise and store.  O^T tile: lane column = query qi, rows = head dim in
