@@ -165,9 +165,9 @@ attn_status last_hip_status() {
 template <bool BF16, int D>
 void launch_fwd_d(const Args& a, bool causal, dim3 grid, hipStream_t st) {
   if (causal)
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, true>), grid, dim3(64 * attn::fwd_waves(D)), 0, st, a);
   else
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, false>), grid, dim3(64 * attn::fwd_waves(D)), 0, st, a);
 }
 
 template <bool BF16>
@@ -272,8 +272,9 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   a.out_o = static_cast<uint16_t*>(o);
   a.lse_out = lse;
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  dim3 grid(p->heads_q * p->batch, (p->seqlen_q + attn::kFwdBM - 1) / attn::kFwdBM, 1);
   const int dt = dtile_for(p->head_dim);
+  const int bm = attn::fwd_bm(dt);
+  dim3 grid(p->heads_q * p->batch, (p->seqlen_q + bm - 1) / bm, 1);
   if (p->dtype == ATTN_BF16) launch_fwd<true>(a, dt, banded(p), grid, hs);
   else launch_fwd<false>(a, dt, banded(p), grid, hs);
   return last_hip_status();

@@ -25,7 +25,10 @@
 
 namespace attn {
 
-constexpr int kFwdBM = 128;  // query rows per workgroup (4 waves x 32)
+// Waves per workgroup, 32 query rows each: 8 (two per SIMD) up to head dim
+// 128, 4 (one per SIMD) for the 256-wide tile.
+constexpr int fwd_waves(int d) { return d > 128 ? 4 : 8; }
+constexpr int fwd_bm(int d) { return 32 * fwd_waves(d); }  // query rows per workgroup
 constexpr int kFwdBN = 64;   // key rows per iteration
 // The running row maximum (log2 units) is moved only when a row grows past it
 // by more than this, so P <= 2^8 = 256: exact in fp32 sums, and within the
@@ -37,17 +40,19 @@ constexpr float kFwdRescaleSlack = 8.f;
 constexpr int fwd_waves_per_simd(int d) { return d > 128 ? 1 : 2; }
 
 template <bool BF16, int D, bool BANDED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(D), fwd_waves_per_simd(D))))
+__global__ __launch_bounds__(64 * fwd_waves(D)) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(D), fwd_waves_per_simd(D))))
 void attn_fwd_kernel(Args a) {
-  constexpr int BM = kFwdBM, BN = kFwdBN;
+  constexpr int NW = fwd_waves(D);
+  constexpr int BM = fwd_bm(D), BN = kFwdBN;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int RB = D * 2;               // bytes per row
   constexpr int TILE = BN * RB;           // one K (or V) block
   constexpr int STAGE = 2 * TILE;         // K then V
-  constexpr int NCH = BN * CPR / 256;     // direct loads per thread per K (or V) block
+  constexpr int NT = 64 * NW;             // threads
+  constexpr int NCH = BN * CPR / NT;      // direct loads per thread per K (or V) block
   constexpr int TK = BN / 32;             // key tiles per block
   constexpr int TD = D / 32;              // head-dim tiles
-  static_assert(BN * CPR % 256 == 0, "tile/thread mismatch");
+  static_assert(BN * CPR % NT == 0, "tile/thread mismatch");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
   const uint32_t smem_lds = lds_addr(smem);
@@ -104,7 +109,7 @@ void attn_fwd_kernel(Args a) {
   int kdma[NCH], vdma[NCH];
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    const int S = (i * 4 + w) * 64 + lane;
+    const int S = (i * NW + w) * 64 + lane;
     const int r = S / CPR;
     const int c = (S % CPR) ^ swz<CPR>(r);
     kdma[i] = 8 * c < hd ? (r * (int)a.k_r + 8 * c) * 2 : kOffOOB;
@@ -116,7 +121,7 @@ void attn_fwd_kernel(Args a) {
     const uint32_t tv = (uint32_t)(nb * BN) * (uint32_t)a.v_r * 2u;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const uint32_t dst = stage + (uint32_t)((i * 4 + w) * 64) * 16u;
+      const uint32_t dst = stage + (uint32_t)((i * NW + w) * 64) * 16u;
       dma16(srdK, kdma[i] == kOffOOB ? kOffOOB : (int)((uint32_t)kdma[i] + tk), dst);
       dma16(srdV, vdma[i] == kOffOOB ? kOffOOB : (int)((uint32_t)vdma[i] + tv), dst + TILE);
     }
