@@ -96,22 +96,41 @@ void attn_bwd_dkdv_kernel(Args a) {
   const int rows_k = min(BN, s.sk - kv0);
 
   // ---- K, V of this wave's 32 key rows as B operands of S = Q K^T and
-  // dP = dO V^T (column = key, k = head dim).  Rows past the end read as 0.
+  // dP = dO V^T (column = key, k = head dim), held in registers for the whole
+  // workgroup.  They come through LDS: the block's K and V tiles are loaded
+  // with direct global->LDS loads (16 contiguous bytes per lane, each row
+  // once) into the region of the last stage and the exchange slots, which
+  // the loop first touches after the first tile, and each wave then reads its
+  // fragments with conflict-free row reads of the swizzled tiles.  Rows past
+  // the end read as 0.
   u32x4 kf[D / 16], vf[D / 16];
-  {
+  constexpr int KVR = (NSTAGE - 1) * STAGE;     // LDS byte offset of the K tile, V follows
+  constexpr int KVI = BN * CPR / (64 * NW);     // direct loads per wave per K (or V) tile
+  static_assert(KVR + 2 * BN * RB <= SINK, "K/V staging fits the last stage and the exchange slots");
+  auto load_kv_lds = [&] {
     const uint16_t* kb = a.k + s.bk * a.k_b + (int64_t)(s.k0 + kv0) * a.k_r + (int64_t)g * a.k_h;
     const uint16_t* vb = a.v + s.bk * a.v_b + (int64_t)(s.k0 + kv0) * a.v_r + (int64_t)g * a.v_h;
-    const rsrc_t rK = make_rsrc(kb, ((int64_t)(rows_k - 1) * a.k_r + hd) * 2);
-    const rsrc_t rV = make_rsrc(vb, ((int64_t)(rows_k - 1) * a.v_r + hd) * 2);
-    const int row = 32 * kvg + c32;
+    const u32x4 srdK = make_srd(kb, ((int64_t)(rows_k - 1) * a.k_r + hd) * 2);
+    const u32x4 srdV = make_srd(vb, ((int64_t)(rows_k - 1) * a.v_r + hd) * 2);
+#pragma unroll
+    for (int i = 0; i < KVI; ++i) {
+      const int S = (i * NW + w) * 64 + lane;
+      const int r = S / CPR;
+      const int c = (S % CPR) ^ swz<CPR>(r);
+      const bool ok = 8 * c < hd;
+      const uint32_t dst = smem_lds + KVR + (uint32_t)((i * NW + w) * 64) * 16u;
+      dma16(srdK, ok ? (r * (int)a.k_r + 8 * c) * 2 : kOffOOB, dst);
+      dma16(srdV, ok ? (r * (int)a.v_r + 8 * c) * 2 : kOffOOB, dst + BN * RB);
+    }
+  };
+  auto read_kv_regs = [&] {
+    const int kvo = KVR + tile_off<CPR>(32 * kvg + c32, 8 * h);
 #pragma unroll
     for (int sd = 0; sd < D / 16; ++sd) {
-      const int d0 = 16 * sd + 8 * h;
-      const bool ok = d0 < hd;
-      kf[sd] = buf_load128(rK, ok ? (row * (int)a.k_r + d0) * 2 : kOffOOB);
-      vf[sd] = buf_load128(rV, ok ? (row * (int)a.v_r + d0) * 2 : kOffOOB);
+      kf[sd] = lds_rd128(smem, kvo ^ (32 * sd));
+      vf[sd] = lds_rd128(smem, (kvo ^ (32 * sd)) + BN * RB);
     }
-  }
+  };
 
   f32x16 dk_acc[TDH], dv_acc[TDH];
 #pragma unroll
@@ -393,6 +412,8 @@ void attn_bwd_dkdv_kernel(Args a) {
       const int n = m_end - m_begin;
       // The previous head's last interval ended with a barrier: every wave is
       // done with its stages.
+      const bool first_head = hq == g * a.group;
+      if (first_head) load_kv_lds();
       prefetch(m_begin, 0, true);
       prefetch(m_begin + 1, 1, n > 1);
       if (grp) {
@@ -403,7 +424,11 @@ void attn_bwd_dkdv_kernel(Args a) {
       } else {
         wait_vmcnt<NPF>();
       }
-      lds_barrier();  // tile 0 landed
+      lds_barrier();  // tile 0 (and K/V) landed
+      if (first_head) {
+        read_kv_regs();
+        lds_barrier();  // every wave has its K/V before the staging region is reused
+      }
       if (grp) lds_barrier();  // interval 0: group 0's phase 1 of tile 0
       int st = 0, st_load = 2;
       for (int j = 0; j < n; ++j) {
@@ -426,9 +451,15 @@ void attn_bwd_dkdv_kernel(Args a) {
       // for at the end of tile j; after its loads a wave issues only tile j's
       // two dS^T stores.
       const int n = m_end - m_begin;
+      const bool first_head = hq == g * a.group;
+      if (first_head) load_kv_lds();
       prefetch(m_begin, 0, true);
       wait_vmcnt<0>();
-      lds_barrier();  // tile 0 landed
+      lds_barrier();  // tile 0 (and K/V) landed
+      if (first_head) {
+        read_kv_regs();
+        lds_barrier();  // every wave has its K/V before the staging region is reused
+      }
       int st = 0;
       for (int j = 0; j < n; ++j) {
         prefetch(m_begin + j + 1, st ^ 1, j + 1 < n);
