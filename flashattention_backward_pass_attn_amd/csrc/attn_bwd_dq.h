@@ -121,11 +121,20 @@ void attn_bwd_dq_kernel(Args a) {
 #pragma unroll
     for (int i = 0; i < SI; ++i) {
       // 16-byte slot S of the tile's dS^T image: key tile S / (NW*128), then
-      // the NW contiguous query-tile chunks of that key tile.
+      // the NW contiguous query-tile chunks of that key tile.  A chunk whose
+      // 32 keys the chunk's 32 queries cannot see was never written: it is
+      // not fetched (zeros land instead; the product skips it anyway).
       const int S0 = (i * NW + w) * 64;
       const int kt = S0 / (NW * 128);
+      const int j = (S0 % (NW * 128)) / 128;  // query tile (wave) of the chunk
+      bool live = true;
+      if (BANDED) {
+        const int k_lo = n * BN + 32 * kt;
+        const int qj = q0 + 32 * j;
+        live = k_lo <= min(s.sk - 1, qj + 31 + off_causal + a.win_r) && k_lo + 31 >= qj + off_causal - a.win_l;
+      }
       const uint32_t off = (uint32_t)((2 * n + kt) * a.ds_nqt) * 2048u + (uint32_t)((S0 % (NW * 128)) * 16 + lane * 16);
-      dma16_nt(srdS, (int)off, stage + S0 * 16);
+      dma16_nt(srdS, live ? (int)off : kOffOOB, stage + S0 * 16);
     }
   };
 
