@@ -13,12 +13,14 @@
 // per tile pair) but keeps dQ in registers, writes it once, and is
 // deterministic by construction (key blocks are summed in ascending order).
 //
-// Both kernels use 8 wave64s (two per SIMD, so one wave's softmax VALU work
-// and LDS reads hide behind the other's matrix-core work).  Each wave owns 32
-// rows of the stationary operand and splits the streamed tile with a partner
-// wave: the pair computes the two halves of the score tile (no duplicated
-// MFMA work), trades their packed probability/gradient operands through LDS,
-// and then each wave accumulates one half of the head dimension.
+// The dK/dV kernel (this file; the dQ kernels are in attn_bwd_dq.h) runs 8
+// wave64s, two per SIMD, in two groups half a tile apart, so that on every
+// SIMD one wave's softmax and products share each interval with the other
+// wave's products.  Each wave owns 32 key rows and splits the streamed query
+// tile with a partner wave: the pair computes the two halves of the score
+// tile (no duplicated MFMA work), trades their packed probability/gradient
+// operands through LDS, and then each wave accumulates one half of the head
+// dimension.
 #pragma once
 
 #include <type_traits>
@@ -36,15 +38,17 @@ constexpr int dkdv_waves(int d) { return d > 128 ? 4 : 8; }
 constexpr int dkdv_bn(int d) { return 16 * dkdv_waves(d); }
 
 // ---------------------------------------------------------------------------
-// dK / dV: one workgroup per (128-key block, KV head, sequence), looping over
-// the query blocks (and, for GQA, over the query heads of the KV head).
+// dK / dV: one workgroup per (key block, KV head, sequence) -- 128 keys, or
+// 64 for the 256-wide head-dim tile -- looping over the query blocks (and,
+// for GQA, over the query heads of the KV head).
 //   wave w: key rows 32*(w>>1) .. +32 of the block, shared with its partner
 //   w^1; query half (w&1) of each 64-query tile for S = Q K^T and
 //   dP = dO V^T; head-dim half (w&1) for dV += P^T dO and dK += dS^T Q.
 //   Waves 0-3 and 4-7 (one of each on every SIMD) run half a tile apart.
-// LDS (D = 128): three stages of {Q, dO, LSE, Delta} (3 x 32.5 KiB,
+// LDS (D = 128): three stages of {Q, dO, LSE*log2(e), -Delta} (3 x 32.5 KiB,
 // swizzled, filled by direct global->LDS loads two tiles ahead) + the P/dS
-// exchange (8 x 4 KiB).
+// exchange (8 x 4 KiB); the block's K and V pass through the last stage and
+// the exchange slots on their way into registers.
 // ---------------------------------------------------------------------------
 template <bool BF16, int D, bool BANDED>
 __global__ __launch_bounds__(64 * dkdv_waves(D)) __attribute__((amdgpu_waves_per_eu(dkdv_waves(D) / 4, dkdv_waves(D) / 4)))
