@@ -237,15 +237,19 @@ void attn_bwd_dkdv_kernel(Args a) {
       // LSE * log2(e) and -Delta of this lane's 16 query rows, in the order
       // of the C layout's rows.  -Delta is the dP accumulator's start value,
       // so the products leave dP - Delta.
+      // (Read after the first S products are issued, so that those start on
+      // the Q operands alone.)
       f32x4 Lr[4];
       f32x16 pacc;
+      auto read_stats = [&] {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        Lr[jj] = *reinterpret_cast<const f32x4*>(sL + 32 * half + 8 * jj + 4 * h);
-        const f32x4 nd = *reinterpret_cast<const f32x4*>(sDl + 32 * half + 8 * jj + 4 * h);
+        for (int jj = 0; jj < 4; ++jj) {
+          Lr[jj] = *reinterpret_cast<const f32x4*>(sL + 32 * half + 8 * jj + 4 * h);
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(sDl + 32 * half + 8 * jj + 4 * h);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pacc[4 * jj + r] = nd[r];
-      }
+          for (int r = 0; r < 4; ++r) pacc[4 * jj + r] = nd[r];
+        }
+      };
 
       // Visibility of the tile's (query, key) pairs (masked tiles only).
       // C layout of S / dP: lane = key column kv_lane, rows = queries
@@ -293,6 +297,7 @@ void attn_bwd_dkdv_kernel(Args a) {
           if (i + PD < 2 * NS) rd(i + PD, i % PD);
           if (i < NS) {
             sacc = mfma32<BF16>(op, kf[i], sacc);
+            if (i == 1) read_stats();
           } else {
             pacc = mfma32<BF16>(op, vf[i - NS], pacc);
             // 16 / NS elements of P per dP product
