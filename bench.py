@@ -1,23 +1,28 @@
 #!/usr/bin/env python3
 """Attention backward benchmark on one MI355X.
 
-One step = one full backward pass (preprocess -> main -> postprocess) over one
-batch of seeded synthetic inputs already resident in HBM; O and LSE come from
-one untimed forward.  Prints ONE JSON line on stdout:
+One step = one full backward pass (preprocess -> dK/dV -> dQ, every kernel of
+the path) over one batch of seeded synthetic inputs already resident in HBM;
+O and LSE come from one untimed forward.  Prints ONE JSON line on stdout:
 
   metric/value/unit    backward TFLOP/s, counted as 10*b*h*Sq*Sk*d (halved
-                       when causal), over the wall clock of K steps bracketed
-                       by torch.cuda.synchronize();
-  roofline             the main kernel (the dominant one) against the MI355X
-                       dense fp16/bf16 matrix-core peak, its duration taken
-                       with HIP events on the launch stream inside the timed
-                       region; HBM traffic from the committed rocprofv3
+                       when causal), over the MEDIAN of K hipEvent-bracketed
+                       attn_bwd calls on the launch stream (the mean and the
+                       wall clock of the K calls, bracketed by
+                       torch.cuda.synchronize(), are reported beside it);
+  roofline             the dominant kernel (dK/dV) against the MI355X dense
+                       fp16/bf16 matrix-core peak, its duration the median of
+                       HIP events around that kernel's launch on the launch
+                       stream; HBM traffic from the committed rocprofv3
                        FETCH_SIZE/WRITE_SIZE measurement when it still matches
                        the kernel source (else null);
+  forward              the forward kernel that supplies O and LSE, timed the
+                       same way (not part of the metric);
   cpu_baseline         the fp64 CPU oracle's backward on a bounded sample of
-                       the same workload (a few heads), scaled to TFLOP/s.
+                       the same workload (whole heads), scaled to TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 40] [--workload NAME]
+       python bench.py --calibrate     (matrix-core / LDS / atomic rates of the box)
 """
 from __future__ import annotations
 
@@ -36,21 +41,22 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 MFMA_PEAK_TFLOPS = {"fp16": 2516.6, "bf16": 2516.6}  # 256 CU x 2.4 GHz x 4096 flop/clk (dense)
-# What flashattention_backward_pass_attn_amd/csrc/mfma_peak.hip sustains on an
-# MI355X with nothing but 32x32x16 products in flight (clock about 1.93 GHz
-# under that load); profiles/mfma_rate_and_valu_overlap_mi355x.md.  Context
-# for the roofline fraction, not its denominator.
-MFMA_MEASURED_TFLOPS = {"fp16": 1905.1, "bf16": 2026.2}
+# What bench_calibrate.hip's products-only loop sustains on an MI355X (8 waves
+# per CU); profiles/calibration_mi355x.md.  Context for the roofline
+# fraction, not its denominator.
+MFMA_MEASURED_TFLOPS = {"fp16": 2469.0, "bf16": 2469.0}
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_backward_pass_attn_amd/csrc/attn_bwd_split.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_bwd_dq.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_device.h"]
 TRAFFIC_FILE = "profiles/bwd_{kernel}_traffic_{workload}.json"
 # Matrix-core work of each gradient kernel, in units of 2*b*h*Sq*Sk*d (halved
-# when causal): dK/dV does S, dP, dV, dK; dQ (over the stored dS, the path the
-# default workspace selects) does dQ only.  The metric counts the method's 5
-# contractions (10*b*h*Sq*Sk*d) for the whole backward.
-KERNEL_UNITS = {"attn_bwd_dkdv_kernel": 4, "attn_bwd_dq_kernel": 1}
+# when causal): dK/dV does S, dP, dV, dK; dQ recomputes S and dP and does dQ.
+# The metric counts the method's 5 contractions (10*b*h*Sq*Sk*d) for the whole
+# backward; the 2 recomputed ones are not counted.
+KERNEL_UNITS = {"attn_bwd_dkdv_kernel": 4, "attn_bwd_dq_kernel": 3}
+# launch name of each gradient kernel's symbol, per head-dim tile
+DQ_SYMBOL = {False: "attn_bwd_dq_recompute_kernel", True: "attn_bwd_dq_wide_kernel"}
 
 
 def log(*a):
@@ -82,6 +88,18 @@ def load_traffic(workload: str, kernel: str):
         log(f"traffic record {path} predates the current kernel source: reporting null")
         return None
     return rec
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline(w: workloads.Workload, inp, budget_s: float):
@@ -124,6 +142,8 @@ def cpu_baseline(w: workloads.Workload, inp, budget_s: float):
         "value": done_flops / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "host_cpu": host_cpu_model(),
+        "host_logical_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{heads} (sequence, query head) pairs of {w.name}, fp64 NumPy backward given the oracle's "
                   f"LSE, {spent:.1f} s; flops counted as for the GPU",
@@ -141,8 +161,10 @@ def _counter_rows(path: str, counter: str):
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter:
-                # "void ns::name<targs>(args)" -> "name"
+                # "void ns::name<targs>(args)" -> "name"; both dQ kernels count as the dQ kernel
                 name = r["Kernel_Name"].split("(")[0].split("<")[0].split()[-1].split("::")[-1]
+                if name in DQ_SYMBOL.values():
+                    name = "attn_bwd_dq_kernel"
                 rows.setdefault(name, []).append(float(r["Counter_Value"]))
     return rows
 
@@ -200,8 +222,12 @@ def main(argv=None):
                          "files (FETCH_SIZE, WRITE_SIZE) of `bench.py --copy-calibration`, then exit")
     ap.add_argument("--traffic-command", default="",
                     help="with --traffic-from: the profiled command, stored in the record")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="build and run bench_calibrate.hip (matrix-core, LDS, vector-overlap and atomic rates)")
     args = ap.parse_args(argv)
 
+    if args.calibrate:
+        return calibrate()
     if args.traffic_from:
         return write_traffic(args.traffic_from[0], args.traffic_from[1], args.workload, args.traffic_command)
     if args.gpus != 1:
@@ -235,22 +261,45 @@ def main(argv=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     p = fa.make_params(q, k, w.causal, scale, args.deterministic, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"),
                        kw.get("max_seqlen_q"), kw.get("max_seqlen_k"))
-    ws = torch.empty(max(fa.bwd_workspace_size(p), 256), dtype=torch.uint8, device=dev)
+    ws_bytes = fa.bwd_workspace_size(p)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     common = dict(causal=w.causal, softmax_scale=scale, deterministic=args.deterministic, dq=dq, dk=dk, dv=dv,
                   workspace=ws, **kw)
     flops = workload_flops(w, inp)
     torch.cuda.synchronize()
 
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2]
+
     for _ in range(args.warmup):
         fa.attn_bwd(q, k, v, o, lse, do, **common)
     torch.cuda.synchronize()
 
+    # Timed region: K full backward calls, each bracketed by HIP events on the
+    # launch stream (the binding launches on torch's current stream).
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        e = ev[i]
+        ev[i][0].record()
+        fa.attn_bwd(q, k, v, o, lse, do, **common)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = [a_.elapsed_time(b_) for a_, b_ in ev]
+    ms_per_step = med(step_ms)
+    ms_mean = sum(step_ms) / K
+    ms_wall = (t1 - t0) * 1e3 / K
+    log(f"{w.name}: step median {ms_per_step:.4f} ms, mean {ms_mean:.4f} ms, wall {ms_wall:.4f} ms per call")
+
+    # Per-kernel durations: the same backward launched phase by phase, with
+    # events between the launches (medians over as many steps).
+    P = max(1, min(K, 50))
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(P)]
+    for i in range(P):
+        e = pev[i]
         e[0].record()
         fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_PREPROCESS, **common)
         e[1].record()
@@ -259,12 +308,21 @@ def main(argv=None):
         fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_DQ, **common)
         e[3].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    pre_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / K
-    dkdv_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / K
-    dq_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / K
-    log(f"{w.name}: step {ms_per_step:.4f} ms (events: pre {pre_ms:.4f} dkdv {dkdv_ms:.4f} dq {dq_ms:.4f} ms)")
+    pre_ms = med([e[0].elapsed_time(e[1]) for e in pev])
+    dkdv_ms = med([e[1].elapsed_time(e[2]) for e in pev])
+    dq_ms = med([e[2].elapsed_time(e[3]) for e in pev])
+    log(f"{w.name}: kernels pre {pre_ms:.4f} dkdv {dkdv_ms:.4f} dq {dq_ms:.4f} ms")
+
+    # The forward that supplies O and LSE (not part of the metric).
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for _ in range(5):
+        fa.attn_fwd(q, k, v, causal=w.causal, softmax_scale=scale, out=o, lse=lse, **kw)
+    for a_, b_ in fev:
+        a_.record()
+        fa.attn_fwd(q, k, v, causal=w.causal, softmax_scale=scale, out=o, lse=lse, **kw)
+        b_.record()
+    torch.cuda.synchronize()
+    fwd_ms = med([a_.elapsed_time(b_) for a_, b_ in fev])
 
     if args.copy_calibration:
         n = 1 << 28  # 256 Mi floats = 1 GiB read + 1 GiB written
@@ -282,20 +340,15 @@ def main(argv=None):
     for name, ms in kernels.items():
         kfl = flops / 5.0 * KERNEL_UNITS[name]
         per_kernel[name] = {"ms": round(ms, 4), "tflops": round(kfl / (ms * 1e-3) / 1e12, 2),
-                            "frac": round(kfl / (ms * 1e-3) / 1e12 / peak, 4), "flop": kfl}
-    # the dQ kernel streams the stored dS (2 bytes per visible (query, key)
-    # pair = 2 * flops / (10 * d)) plus K and dQ once: HBM-bound
-    elem = 2
-    k_bytes = elem * w.head_dim * (int(inp["lengths_k"].sum()) * w.heads_kv if w.varlen
-                                   else w.batch * w.seqlen * w.heads_kv)
-    q_bytes = elem * w.head_dim * (int(inp["lengths_q"].sum()) * w.heads_q if w.varlen
-                                   else w.batch * w.seqlen * w.heads_q)
-    dq_bytes = elem * flops / (10.0 * w.head_dim) + k_bytes + q_bytes
-    per_kernel["attn_bwd_dq_kernel"].update({
-        "bound": "hbm", "bytes": dq_bytes,
-        "gbs": round(dq_bytes / (dq_ms * 1e-3) / 1e9, 1),
-        "hbm_frac": round(dq_bytes / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
-    per_kernel["attn_bwd_dkdv_kernel"]["bound"] = "mfma"
+                            "frac": round(kfl / (ms * 1e-3) / 1e12 / peak, 4), "flop": kfl, "bound": "mfma",
+                            "contractions": KERNEL_UNITS[name]}
+    per_kernel["attn_bwd_dq_kernel"]["symbol"] = DQ_SYMBOL[w.head_dim > 128]
+    # preprocess: reads O and dO (2*d*2 bytes per row) and LSE, writes -Delta
+    # and LSE*log2(e): 4d + 12 bytes per (query head, row)
+    rows = (int(inp["lengths_q"].sum()) if w.varlen else w.batch * w.seqlen) * w.heads_q
+    pre_bytes = rows * (4 * w.head_dim + 12)
+    per_kernel["attn_bwd_pre_kernel"] = {"ms": round(pre_ms, 4), "bound": "hbm", "bytes": pre_bytes,
+                                         "gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1)}
     dom = max(kernels, key=kernels.get)
     traffic = load_traffic(w.name, dom.replace("attn_bwd_", "").replace("_kernel", ""))
     roofline = {
@@ -308,10 +361,13 @@ def main(argv=None):
         "kernel": dom,
         "kernel_ms": per_kernel[dom]["ms"],
         "kernels": per_kernel,
-        "preprocess_ms": round(pre_ms, 4),
         "measured_peak": MFMA_MEASURED_TFLOPS[w.dtype],
         "frac_of_measured_peak": round(per_kernel[dom]["tflops"] / MFMA_MEASURED_TFLOPS[w.dtype], 4),
     }
+    fwd_flops = flops * 0.4  # S = Q K^T and O = P V: 4*b*h*Sq*Sk*d, halved when causal
+    forward = {"ms": round(fwd_ms, 4), "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+               "frac": round(fwd_flops / (fwd_ms * 1e-3) / 1e12 / peak, 4), "flop": fwd_flops,
+               "kernel": "attn_fwd_kernel", "bound": "mfma"}
     cpu = None
     if args.cpu_baseline_seconds > 0:
         log("cpu baseline: timing the oracle backward on a bounded sample ...")
@@ -319,7 +375,7 @@ def main(argv=None):
     cfg = {"workload": w.name, "dtype": w.dtype, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
            "seqlen": (int(inp["lengths_q"].max()) if w.varlen else w.seqlen), "head_dim": w.head_dim,
            "causal": w.causal, "varlen": w.varlen, "deterministic": args.deterministic,
-           "flop_per_step": flops, "parallelism": "single GPU"}
+           "flop_per_step": flops, "workspace_bytes": ws_bytes, "parallelism": "single GPU"}
     if w.varlen:
         cfg["lengths"] = [int(x) for x in inp["lengths_q"]]
     rec = {
@@ -330,6 +386,9 @@ def main(argv=None):
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_mean": round(ms_mean, 4),
+        "ms_per_step_wall": round(ms_wall, 4),
+        "timing": "median of K hipEvent-bracketed attn_bwd calls on the launch stream",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -338,10 +397,28 @@ def main(argv=None):
         "config": cfg,
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "roofline": roofline,
+        "forward": forward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
     return 0
+
+
+def calibrate() -> int:
+    """Build bench_calibrate.hip with hipcc and run it (prints its table)."""
+    import shutil
+    import subprocess
+    import tempfile
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    src = os.path.join(ROOT, "bench_calibrate.hip")
+    out = os.path.join(tempfile.mkdtemp(prefix="attn_calibrate_"), "calibrate")
+    cmd = [hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", src, "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        return res.returncode
+    return subprocess.run([out]).returncode
 
 
 if __name__ == "__main__":

@@ -23,8 +23,8 @@ ATTN_ERR_HIP = 4
 ATTN_FP16 = 0
 ATTN_BF16 = 1
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd_workspace_size", "attn_bwd_workspace_size_min", "attn_bwd",
-                    "attn_bwd_phases", "attn_status_string", "attn_version")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_phases", "attn_status_string",
+                    "attn_version")
 PHASE_PREPROCESS = 1
 PHASE_DKDV = 2
 PHASE_DQ = 4
@@ -89,8 +89,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_bwd_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.attn_bwd_workspace_size.restype = ctypes.c_int
-    lib.attn_bwd_workspace_size_min.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
-    lib.attn_bwd_workspace_size_min.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd_phases.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp,
@@ -201,26 +199,24 @@ def attn_fwd(q, k, v, causal: bool = False, softmax_scale: Optional[float] = Non
     return out, lse
 
 
-def bwd_workspace_size(p: attn_params, minimal: bool = False) -> int:
-    """Workspace bytes of the fast path (Delta + stored dS), or with ``minimal``
-    the smallest accepted workspace (row statistics only; dQ then recomputes dS)."""
+def bwd_workspace_size(p: attn_params) -> int:
+    """Workspace bytes attn_bwd needs: Delta and LSE*log2(e), fp32, O(Sq) per head."""
     n = ctypes.c_size_t(0)
     lib = load_library()
-    fn = lib.attn_bwd_workspace_size_min if minimal else lib.attn_bwd_workspace_size
-    _check(fn(ctypes.byref(p), ctypes.byref(n)), "attn_bwd_workspace_size")
+    _check(lib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)), "attn_bwd_workspace_size")
     return n.value
 
 
 def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optional[float] = None,
              deterministic: bool = False, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
              max_seqlen_k=None, dq=None, dk=None, dv=None, workspace=None, return_delta: bool = False,
-             phases: int = PHASE_ALL, minimal_workspace: bool = False, window=(-1, -1)):
+             phases: int = PHASE_ALL, window=(-1, -1)):
     """dQ, dK, dV (and optionally Delta) of sum(O * dO) for attention.
 
     ``phases`` selects which of the three kernels to launch (see attn_bwd_phases
     in include/attn.h); the default launches all of them.  Without a
-    ``workspace`` one is allocated: the fast path's size, or with
-    ``minimal_workspace`` the smallest accepted one (dQ then recomputes dS).
+    ``workspace`` one of ``bwd_workspace_size()`` bytes is allocated (two fp32
+    row statistics per query row and head).
     """
     torch = _torch()
     lib = load_library()
@@ -233,7 +229,7 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optiona
     dv = torch.empty_like(v) if dv is None else dv
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         setattr(p, name, _strides(t, varlen))
-    need = bwd_workspace_size(p, minimal=minimal_workspace)
+    need = bwd_workspace_size(p)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     delta = torch.empty_like(lse) if return_delta else None

@@ -16,9 +16,8 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 SOURCES = [os.path.join(CSRC, "attn_api.hip")]
-HEADERS = [os.path.join(CSRC, f) for f in ("attn_device.h", "attn_fwd.h", "attn_bwd.h")] + [
-    os.path.join(ROOT, "include", "attn.h")
-]
+HEADERS = [os.path.join(CSRC, f) for f in ("attn_device.h", "attn_fwd.h", "attn_bwd.h", "attn_bwd_split.h",
+                                              "attn_bwd_dq.h")] + [os.path.join(ROOT, "include", "attn.h")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -26,7 +25,6 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
-    "-munsafe-fp-atomics",
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",

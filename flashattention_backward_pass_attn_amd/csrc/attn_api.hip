@@ -9,7 +9,8 @@
 // run_flash_bwd: the preprocess first, then the gradient kernels, all on the
 // caller's stream.  Here the gradients come from two kernels (dK/dV
 // KV-stationary, dQ Q-stationary) instead of one kernel with fp32 dQ atomics
-// plus a dQ postprocess; see attn_bwd_split.h for why.
+// plus a dQ postprocess; see attn_bwd_split.h for why.  The only workspace is
+// O(Sq) per head: Delta and LSE * log2(e).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -88,35 +89,14 @@ int64_t stat_count(const attn_params* p) {
                       : (int64_t)p->batch * p->heads_q * p->seqlen_q;
 }
 
-// One fp32 row statistic laid out like lse, and the workspace's statistics
-// region: Delta, then LSE * log2(e) (both written by the preprocess).
+// One fp32 row statistic laid out like lse, and the workspace: Delta, then
+// LSE * log2(e) (both written by the preprocess), each rounded up to 256
+// bytes.  That is all the backward needs: the gradient kernels recompute P
+// and dS tile by tile and keep dQ in registers.
 size_t stat_bytes(const attn_params* p) {
   return round_up((size_t)stat_count(p) * sizeof(float), kAlign);
 }
-size_t delta_bytes(const attn_params* p) { return 2 * stat_bytes(p); }
-
-// dS^T chunk grid (see Args::ds): 4 key-tile slots per 128-key block of each
-// sequence plus 4 per sequence for the ragged blocks, and query tiles in
-// pairs (the dK/dV kernel writes 64-query tiles).
-int64_t ds_nkt(const attn_params* p) {
-  const int64_t rows_k = is_varlen(p) ? (int64_t)p->total_k : (int64_t)p->batch * p->seqlen_k;
-  return 4 * (rows_k / 128) + 4 * (int64_t)p->batch + 4;
-}
-int32_t ds_nqt(const attn_params* p) { return 2 * ((p->seqlen_q + 63) / 64); }
-
-size_t ds_bytes(const attn_params* p) {
-  return round_up((size_t)p->heads_q * (size_t)ds_nkt(p) * (size_t)ds_nqt(p) * 2048u, kAlign);
-}
-
-// Full workspace: the statistics then the dS^T chunks (the dQ kernel is then
-// a plain product over them).  Minimal workspace: the statistics only (the dQ
-// kernel then recomputes dS).
-size_t workspace_bytes(const attn_params* p) { return delta_bytes(p) + ds_bytes(p); }
-// Head dims above 128 have only the stored-dS path: their minimum is the full
-// workspace.
-size_t workspace_bytes_min(const attn_params* p) {
-  return p->head_dim > 128 ? workspace_bytes(p) : delta_bytes(p);
-}
+size_t workspace_bytes(const attn_params* p) { return 2 * stat_bytes(p); }
 
 Args make_args(const attn_params* p) {
   Args a;
@@ -194,21 +174,17 @@ void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, d
   if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, D>(a, causal, grid_kv, st);
   if (phases & ATTN_PHASE_DQ) {
     const dim3 blk(64 * attn::kDqWaves);
-    if (a.ds != nullptr) {  // dS^T written by the dK/dV kernel: plain product
-      if (causal)
-        hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, true>), grid_q, blk, 0, st, a);
-      else
-        hipLaunchKernelGGL((attn::attn_bwd_dq_kernel<BF16, D, false>), grid_q, blk, 0, st, a);
-    } else {  // minimal workspace: recompute dS
-      if (causal)
-        hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, true>), grid_q, blk, 0, st, a);
-      else
-        hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, false>), grid_q, blk, 0, st, a);
-    }
+    if (causal)
+      hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, true>), grid_q, blk, 0, st, a);
+    else
+      hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, false>), grid_q, blk, 0, st, a);
   }
 }
 
 int dtile_for(int head_dim) { return head_dim <= 64 ? 64 : (head_dim <= 128 ? 128 : 256); }
+
+// Query rows per dQ workgroup for a head-dim tile.
+int dq_rows(int dtile) { return dtile == 256 ? attn::kDqWideBM : attn::kDqBM; }
 
 template <bool BF16>
 void launch_grads(const Args& a, int dtile, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q,
@@ -218,21 +194,12 @@ void launch_grads(const Args& a, int dtile, bool causal, unsigned phases, dim3 g
   } else if (dtile == 128) {
     launch_grads_d<BF16, 128>(a, causal, phases, grid_kv, grid_q, st);
   } else {
-    // 256-wide tile: dK/dV in one kernel; dQ = dS K is column-separable, so
-    // the stored-dS product runs once per 128-wide half of the head dim (K
-    // and dQ offset by 128 elements, the second half's width the rest).
     if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, 256>(a, causal, grid_kv, st);
     if (phases & ATTN_PHASE_DQ) {
-      Args lo = a, hi = a;
-      lo.head_dim = 128;
-      hi.head_dim = a.head_dim - 128;
-      hi.k = a.k + 128;
-      hi.dq = a.dq + 128;
-      launch_grads_d<BF16, 128>(lo, causal, ATTN_PHASE_DQ, grid_kv, grid_q, st);
-      if (dtile_for(hi.head_dim) == 64)
-        launch_grads_d<BF16, 64>(hi, causal, ATTN_PHASE_DQ, grid_kv, grid_q, st);
+      if (causal)
+        hipLaunchKernelGGL((attn::attn_bwd_dq_wide_kernel<BF16, true>), grid_q, dim3(256), 0, st, a);
       else
-        launch_grads_d<BF16, 128>(hi, causal, ATTN_PHASE_DQ, grid_kv, grid_q, st);
+        hipLaunchKernelGGL((attn::attn_bwd_dq_wide_kernel<BF16, false>), grid_q, dim3(256), 0, st, a);
     }
   }
 }
@@ -288,14 +255,6 @@ attn_status attn_bwd_workspace_size(const attn_params* p, size_t* bytes) {
   return ATTN_OK;
 }
 
-attn_status attn_bwd_workspace_size_min(const attn_params* p, size_t* bytes) {
-  attn_status st = validate_common(p);
-  if (st != ATTN_OK) return st;
-  if (!bytes) return ATTN_ERR_INVALID_ARGUMENT;
-  *bytes = workspace_bytes_min(p);
-  return ATTN_OK;
-}
-
 attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, const void* v,
                             const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                             void* workspace, size_t workspace_bytes_given, float* delta_out, void* stream,
@@ -314,12 +273,7 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return ATTN_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return ATTN_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes_given < workspace_bytes_min(p)) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  // the stored-dS path addresses one head's dS tiles with 32-bit offsets
-  const bool ds_fits = (int64_t)(4 * ((p->seqlen_k + 127) / 128) + 4) * ds_nqt(p) * 2048 < ((int64_t)1 << 30);
-  const bool use_ds = ds_fits && workspace_bytes_given >= workspace_bytes(p);
-  // head dims above 128 have no recompute path for dQ
-  if (p->head_dim > 128 && !use_ds) return ds_fits ? ATTN_ERR_WORKSPACE_TOO_SMALL : ATTN_ERR_UNSUPPORTED;
+  if (workspace_bytes_given < workspace_bytes(p)) return ATTN_ERR_WORKSPACE_TOO_SMALL;
 
   Args a = make_args(p);
   a.q = static_cast<const uint16_t*>(q);
@@ -334,12 +288,6 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   a.delta_out = delta_out;
   a.delta = static_cast<float*>(workspace);
   a.lse2 = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + stat_bytes(p));
-  if (use_ds) {
-    a.ds = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(workspace) + delta_bytes(p));
-    a.ds_bytes = (int64_t)ds_bytes(p);
-    a.ds_nkt = ds_nkt(p);
-    a.ds_nqt = ds_nqt(p);
-  }
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const bool bf = p->dtype == ATTN_BF16;
@@ -356,7 +304,7 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   unsigned grad_phases = phases & (ATTN_PHASE_DKDV | ATTN_PHASE_DQ);
   const int kvbn = attn::dkdv_bn(dt);
   const int kvblocks = (p->seqlen_k + kvbn - 1) / kvbn;
-  const int dqblocks = (p->seqlen_q + attn::kDqBM - 1) / attn::kDqBM;
+  const int dqblocks = (p->seqlen_q + dq_rows(dt) - 1) / dq_rows(dt);
   if (kvblocks == 0) grad_phases &= ~ATTN_PHASE_DKDV;  // no keys: nothing to write in dK/dV
   if (dqblocks == 0) grad_phases &= ~ATTN_PHASE_DQ;    // no queries: no dQ rows
   if (grad_phases) {

@@ -1,26 +1,19 @@
-// Attention backward on gfx950: the dQ kernel.
+// Attention backward on gfx950: the dQ kernels.
 //
 // dQ = scale * dS K (tilelang test_tilelang_kernel_mha_bwd.py, flashattn_bwd:
 // the dQ contribution of each key block is dS K; the Hopper
 // flash_bwd_launch_template.h page applies the softmax scale to dQ after the
-// sum over key blocks).  dS = P o (dP - Delta) is not recomputed here: the
-// dK/dV kernel, which forms it anyway, writes it to the workspace as bf16 /
-// fp16 dS^T chunks (32 keys x 32 queries, 2 KiB, rows = keys, 64 bytes per
-// row holding query runs 4h + 8r .. +3 at byte 32h + 8r), and this kernel
-// is a plain matrix product over them, summed over key blocks in ascending
-// order in registers -- no atomics, so the result is deterministic.
-//
-// Work: one workgroup per (query head x sequence, 256-query block), 8 waves,
-// wave w owning queries 32w .. +32 of the block.  Each 64-key tile brings
-// the block's dS^T chunks (2 key tiles x 8 query tiles, 32 KiB) and the K
-// tile (swizzled like the other kernels' K tiles) into LDS by direct
-// global->LDS loads, two tiles ahead in three stages; the kernel streams the
-// dS workspace from HBM and is bound by that read.  Per 16-key step the dS
-// A operand (query rows, keys as k) and the K B operand (keys as k,
-// head-dim columns) are both transpose reads, which apply the same key
-// permutation to both operands.  Chunks a wave's queries cannot see (above
-// its causal diagonal or past the last key) were never written: their A
-// operand is replaced by zeros.
+// sum over key blocks).  The kernels are Q-stationary: a wave keeps its
+// queries' Q and dO in registers, streams K and V tiles through LDS,
+// recomputes S^T = K Q^T and dP^T = V dO^T per key tile, forms
+// dS^T = P^T o (dP^T - Delta) with P = exp2(S*scale*log2e - LSE*log2e) from
+// the saved LSE, and accumulates dQ in registers over the key tiles in
+// ascending order -- no atomics and no dQ accumulator in memory, so the
+// result is deterministic and the only workspace is the two row statistics.
+// The transposed score tile puts one query per lane, so LSE and Delta are
+// per-lane constants, and dS^T leaves the MFMA in the A-operand layout of
+// dQ = dS K.  The softmax scale is applied once, in the epilogue, which is
+// the pages' dQ postprocess (scale, convert) fused.
 #pragma once
 
 #include <type_traits>
@@ -29,173 +22,11 @@
 
 namespace attn {
 
-constexpr int kDqWaves = 8;              // waves per dQ workgroup (32 queries each)
+constexpr int kDqWaves = 8;              // waves per dQ workgroup (32 queries each), head dim <= 128
 constexpr int kDqBM = 32 * kDqWaves;     // query rows per dQ workgroup
 constexpr int kDqBN = 64;                // key rows per tile
-constexpr int kDqPD = 6;                 // recompute kernel: LDS reads in flight ahead of their MFMAs
-
-template <bool BF16, int D, bool BANDED>
-__global__ __launch_bounds__(64 * kDqWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void attn_bwd_dq_kernel(Args a) {
-  constexpr int NW = kDqWaves;
-  constexpr int BM = kDqBM, BN = kDqBN;
-  constexpr int CPR = D / 8;
-  constexpr int RB = D * 2;
-  constexpr int KT = BN * RB;                // bytes of a K tile
-  constexpr int DST = 2 * NW * 2048;         // bytes of the dS^T chunks of a tile
-  constexpr int STAGE = DST + KT;
-  constexpr int NSTAGE = 3;
-  constexpr int TD = D / 32;                 // head-dim tiles of dQ
-  constexpr int KI = BN * CPR / (64 * NW);   // direct loads per wave per K tile
-  constexpr int SI = DST / 16 / (64 * NW);   // direct loads per wave per dS^T tile
-  static_assert(TD >= 2 && KI >= 1 && SI >= 1, "head dim of 64 or 128");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
-  const uint32_t smem_lds = lds_addr(smem);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = wave_id();
-  const int h = lane >> 5;
-  const int c32 = lane & 31;
-  const int sl = lane & 15;
-  const int gg = lane >> 4;
-  const int rr = sl >> 2;
-  const int tcol = 16 * (gg & 1) + 4 * (sl & 3);
-  // grid (query head x sequence, query block): the longest causal blocks of
-  // every head start first, and one head's blocks share an XCD.
-  const int hq = blockIdx.x % a.heads_q;
-  const int z = blockIdx.x / a.heads_q;
-  const Seq s = seq_info(a, z);
-  const int mb = BANDED ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
-  const int q0 = mb * BM;
-  if (q0 >= s.sq) return;
-  const int hd = a.head_dim;
-  const int g = hq / a.group;
-  const int off_causal = s.sk - s.sq;
-  const int qw = q0 + 32 * w;  // first query of this wave
-
-  // Key tiles this query block sees.
-  int n_begin = 0, n_end = (s.sk + BN - 1) / BN;
-  if (BANDED) {
-    const Range kr = band_keys(a, q0, min(q0 + BM, s.sq) - 1, s.sq, s.sk);
-    n_begin = kr.lo / BN;
-    n_end = kr.hi < kr.lo ? n_begin : kr.hi / BN + 1;
-  }
-  // Keys this wave's queries see (chunks wholly outside were never written).
-  int kw_hi = s.sk - 1, kw_lo = -kWinInf;
-  if (BANDED) {
-    kw_hi = min(kw_hi, qw + 31 + off_causal + a.win_r);
-    kw_lo = qw + off_causal - a.win_l;
-  }
-
-  f32x16 dq_acc[TD];
-#pragma unroll
-  for (int t = 0; t < TD; ++t) dq_acc[t] = f32x16{};
-
-  // ---- direct loads.  K rows: swizzled 16-byte chunks as in the other
-  // kernels.  dS^T: for each of the tile's two 32-key tiles, the block's 8
-  // query-tile chunks are contiguous in the workspace (16 KiB), copied as is.
-  auto slot_off = [&](int S, int row_stride) {
-    const int r = S / CPR;
-    const int c = (S % CPR) ^ swz<CPR>(r);
-    return 8 * c < hd ? (r * row_stride + 8 * c) * 2 : kOffOOB;
-  };
-  int kdma[KI];
-#pragma unroll
-  for (int i = 0; i < KI; ++i) kdma[i] = slot_off((i * NW + w) * 64 + lane, (int)a.k_r);
-  const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
-  // One descriptor for the head's K rows and one for this block's dS^T
-  // chunks (from key slot 0, query tile q0/32 on); a tile is a 32-bit lane
-  // offset into them (extents below 1 GiB, checked on the host).  K rows
-  // past the end and columns past head_dim read as zero.
-  const u32x4 srdK = make_srd(kbase, ((int64_t)(s.sk - 1) * a.k_r + hd) * 2);
-  const int64_t ds_base = (((int64_t)hq * a.ds_nkt + ds_key_slot0(a, z)) * a.ds_nqt + q0 / 32) * 2048;
-  const u32x4 srdS = make_srd(reinterpret_cast<const uint8_t*>(a.ds) + ds_base, a.ds_bytes - ds_base);
-
-  auto prefetch = [&](int n) {
-    const uint32_t stage = smem_lds + (n % NSTAGE) * STAGE;
-    const uint32_t tk = (uint32_t)(n * BN) * (uint32_t)a.k_r * 2u;
-#pragma unroll
-    for (int i = 0; i < KI; ++i) dma16(srdK, (int)((uint32_t)kdma[i] + tk), stage + DST + ((i * NW + w) * 64) * 16);
-#pragma unroll
-    for (int i = 0; i < SI; ++i) {
-      // 16-byte slot S of the tile's dS^T image: key tile S / (NW*128), then
-      // the NW contiguous query-tile chunks of that key tile.  A chunk whose
-      // 32 keys the chunk's 32 queries cannot see was never written: it is
-      // not fetched (zeros land instead; the product skips it anyway).
-      const int S0 = (i * NW + w) * 64;
-      const int kt = S0 / (NW * 128);
-      const int j = (S0 % (NW * 128)) / 128;  // query tile (wave) of the chunk
-      bool live = true;
-      if (BANDED) {
-        const int k_lo = n * BN + 32 * kt;
-        const int qj = q0 + 32 * j;
-        live = k_lo <= min(s.sk - 1, qj + 31 + off_causal + a.win_r) && k_lo + 31 >= qj + off_causal - a.win_l;
-      }
-      const uint32_t off = (uint32_t)((2 * n + kt) * a.ds_nqt) * 2048u + (uint32_t)((S0 % (NW * 128)) * 16 + lane * 16);
-      dma16_nt(srdS, live ? (int)off : kOffOOB, stage + S0 * 16);
-    }
-  };
-
-  // Transpose-read offsets.  dS^T chunk: key rows 4h + rr (+8) of a 16-key
-  // step, query run starting at tcol (run tcol/8 of half (tcol/4) & 1).
-  const int ds_col = 32 * ((tcol >> 2) & 1) + 8 * (tcol >> 3);
-  const int da = (4 * h + rr) * 64 + ds_col;
-  const int db = (4 * h + rr + 8) * 64 + ds_col;
-  // K tile: key rows 4h + rr (+8), head-dim columns 32t + tcol.
-  const int ka = tile_off<CPR>(4 * h + rr, tcol);
-  const int kb = tile_off<CPR>(4 * h + rr + 8, tcol);
-
-  if (n_begin < n_end) prefetch(n_begin);
-  if (n_begin + 1 < n_end) prefetch(n_begin + 1);
-  for (int n = n_begin; n < n_end; ++n) {
-    if (n + 1 < n_end) {
-      wait_vmcnt<KI + SI>();  // tile n landed (tile n+1 may still be in flight)
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // everyone's loads of tile n; all reads of tile n-1 retired
-    if (n + 2 < n_end) prefetch(n + 2);
-    const uint8_t* st = smem + (n % NSTAGE) * STAGE;
-    const uint8_t* sK = st + DST;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      // this wave's chunk of 32-key tile kt: unwritten if outside the band
-      const bool live = n * BN + 32 * kt <= kw_hi && n * BN + 32 * kt + 31 >= kw_lo;
-      const uint8_t* chunk = st + (kt * NW + w) * 2048;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 aop = tr_frag_b(chunk, da + 16 * s2 * 64, db + 16 * s2 * 64);
-        if (!live) aop = u32x4{0u, 0u, 0u, 0u};
-        const int ro = (32 * kt + 16 * s2) * RB;
-        u32x4 bop[TD];
-#pragma unroll
-        for (int t = 0; t < TD; ++t) bop[t] = tr_frag_b(sK, (ka ^ (64 * t)) + ro, (kb ^ (64 * t)) + ro);
-#pragma unroll
-        for (int t = 0; t < TD; ++t) dq_acc[t] = mfma32<BF16>(aop, bop[t], dq_acc[t]);
-      }
-    }
-  }
-
-  // ---- dQ * scale, converted (round to nearest even).  C layout: lane =
-  // head-dim column, rows = queries 32*w + 8*(j/4) + 4*h + j%4.
-  {
-    const int rows = min(BM, s.sq - q0);
-    const uint16_t* dqb = a.dq + s.bq * a.dq_b + (int64_t)(s.q0 + q0) * a.dq_r + (int64_t)hq * a.dq_h;
-    const rsrc_t rDQ = make_rsrc(dqb, ((int64_t)(rows - 1) * a.dq_r + hd) * 2);
-#pragma unroll
-    for (int t = 0; t < TD; ++t) {
-      const int d = 32 * t + c32;
-      const bool ok = d < hd;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qr = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
-        buf_store_u16(rDQ, ok ? (qr * (int)a.dq_r + d) * 2 : kOffOOB, to_bits<BF16>(dq_acc[t][j] * a.scale));
-      }
-    }
-  }
-}
+constexpr int kDqPD = 6;                 // LDS reads in flight ahead of their MFMAs
+constexpr int kDqWideBM = 128;           // query rows per dQ workgroup, 256-wide head-dim tile
 
 // Slot layout of one key tile of the dQ kernel and where each softmax
 // element's three dependent stages (F, E, M) go.  Slots:
@@ -236,13 +67,9 @@ struct DqSchedule {
 };
 
 // ---------------------------------------------------------------------------
-// dQ without the dS^T workspace (the path taken when the caller's workspace
-// holds only Delta): the kernel recomputes S^T = K Q^T and dP^T = V dO^T per
-// key tile and forms dS^T itself.  Same grid and query ownership as the
-// kernel above; each wave works every 64-key tile alone as two 32-key halves.
-// The transposed score tile puts one query per lane, so LSE and Delta are
-// per-lane constants, and dS^T leaves the MFMA in the A-operand layout of
-// dQ = dS K.
+// dQ for head dims up to 128: one workgroup per (query head x sequence,
+// 256-query block), 8 waves (two per SIMD), wave w owning queries 32w .. +32
+// of the block; each wave works every 64-key tile alone as two 32-key halves.
 //
 // Schedule.  The matrix-core work of one tile is a stream of slots
 //   A: S, dP of half 0      B: dQ of the previous tile's half 1
@@ -579,5 +406,183 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// dQ for the 256-wide head-dim tile (head dims 136 .. 256): one workgroup per
+// (query head x sequence, 128-query block), 4 waves (one per SIMD), wave w
+// owning queries 32w .. +32.  The lane's Q and dO (its column of S^T) stay in
+// registers as B operands (128 registers), dQ accumulates in 8 head-dim tiles
+// (128 accumulation registers).  Key tiles of 32 keys (K and V, 32 KiB) pass
+// through two LDS stages, loaded one tile ahead by direct global->LDS loads.
+// Per tile: S^T and dP^T (alternating head-dim steps), dS^T on the vector
+// ALU, then dQ += dS K; the compiler interleaves the straight-line body.
+// (A software-pipelined version that ran the previous tile's dQ products
+// under this tile's softmax needed more registers than one wave has and
+// spilled.)
+// ---------------------------------------------------------------------------
+template <bool BF16, bool BANDED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_bwd_dq_wide_kernel(Args a) {
+  constexpr int D = 256, NW = 4, BM = 32 * NW, BN = 32;
+  static_assert(BM == kDqWideBM, "grid rows");
+  constexpr int CPR = D / 8, RB = D * 2;
+  constexpr int KT = BN * RB;                 // bytes of a K (or V) tile
+  constexpr int STAGE = 2 * KT;
+  constexpr int NSTAGE = 2;
+  constexpr int TD = D / 32;                  // head-dim tiles of dQ
+  constexpr int NSD = D / 16;                 // k-steps of S^T / dP^T
+  constexpr int KI = BN * CPR / (64 * NW);    // direct loads per wave per K (or V) tile
+  static_assert(KI >= 1 && NSTAGE * STAGE <= 160 * 1024, "tile shape");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  const uint32_t smem_lds = lds_addr(smem);
+
+  const int lane = threadIdx.x & 63;
+  const int w = wave_id();
+  const int h = lane >> 5;
+  const int c32 = lane & 31;
+  const int sl = lane & 15;
+  const int gg = lane >> 4;
+  const int rr = sl >> 2;
+  const int tcol = 16 * (gg & 1) + 4 * (sl & 3);
+  const int hq = blockIdx.x % a.heads_q;
+  const int z = blockIdx.x / a.heads_q;
+  const Seq s = seq_info(a, z);
+  const int mb = BANDED ? (int)(gridDim.y - 1 - blockIdx.y) : (int)blockIdx.y;
+  const int q0 = mb * BM;
+  if (q0 >= s.sq) return;
+  const int hd = a.head_dim;
+  const int g = hq / a.group;
+  const int off_causal = s.sk - s.sq;
+  const int qw = q0 + 32 * w;
+  const int qi = qw + c32;
+
+  u32x4 qf[NSD], df[NSD];
+  float L2, Dl;
+  {
+    const int rows = min(BM, s.sq - q0);
+    const uint16_t* qb = a.q + s.bq * a.q_b + (int64_t)(s.q0 + q0) * a.q_r + (int64_t)hq * a.q_h;
+    const uint16_t* db = a.dout + s.bq * a.do_b + (int64_t)(s.q0 + q0) * a.do_r + (int64_t)hq * a.do_h;
+    const rsrc_t rQ = make_rsrc(qb, ((int64_t)(rows - 1) * a.q_r + hd) * 2);
+    const rsrc_t rO = make_rsrc(db, ((int64_t)(rows - 1) * a.do_r + hd) * 2);
+    const int row = 32 * w + c32;
+#pragma unroll
+    for (int sd = 0; sd < NSD; ++sd) {
+      const int d0 = 16 * sd + 8 * h;
+      const bool ok = d0 < hd;
+      qf[sd] = buf_load128(rQ, ok ? (row * (int)a.q_r + d0) * 2 : kOffOOB);
+      df[sd] = buf_load128(rO, ok ? (row * (int)a.do_r + d0) * 2 : kOffOOB);
+    }
+    const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h + q0;
+    L2 = buf_load_f32(make_rsrc(a.lse2 + st0, (int64_t)rows * 4), row * 4);
+    Dl = buf_load_f32(make_rsrc(a.delta + st0, (int64_t)rows * 4), row * 4);  // -Delta
+  }
+
+  f32x16 dq_acc[TD];
+#pragma unroll
+  for (int t = 0; t < TD; ++t) dq_acc[t] = f32x16{};
+
+  const int svb = tile_off<CPR>(c32, 8 * h);
+  const int tab = tile_off<CPR>(4 * h + rr, tcol);
+  const int tbb = tile_off<CPR>(4 * h + rr + 8, tcol);
+
+  auto slot_off = [&](int S, int row_stride) {
+    const int r = S / CPR;
+    const int c = (S % CPR) ^ swz<CPR>(r);
+    return 8 * c < hd ? (r * row_stride + 8 * c) * 2 : kOffOOB;
+  };
+  int kdma[KI], vdma[KI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int S = (i * NW + w) * 64 + lane;
+    kdma[i] = slot_off(S, (int)a.k_r);
+    vdma[i] = slot_off(S, (int)a.v_r);
+  }
+
+  int n_begin = 0, n_end = (s.sk + BN - 1) / BN;
+  if (BANDED) {
+    const Range kr = band_keys(a, q0, min(q0 + BM, s.sq) - 1, s.sq, s.sk);
+    n_begin = kr.lo / BN;
+    n_end = kr.hi < kr.lo ? n_begin : kr.hi / BN + 1;
+  }
+  const uint16_t* kbase = a.k + s.bk * a.k_b + (int64_t)s.k0 * a.k_r + (int64_t)g * a.k_h;
+  const uint16_t* vbase = a.v + s.bk * a.v_b + (int64_t)s.k0 * a.v_r + (int64_t)g * a.v_h;
+  auto prefetch = [&](int n) {
+    const int rows = min(BN, s.sk - n * BN);
+    const uint32_t stage = smem_lds + (n % NSTAGE) * STAGE;
+    const u32x4 srdK = make_srd(kbase + (int64_t)n * BN * a.k_r, ((int64_t)(rows - 1) * a.k_r + hd) * 2);
+    const u32x4 srdV = make_srd(vbase + (int64_t)n * BN * a.v_r, ((int64_t)(rows - 1) * a.v_r + hd) * 2);
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int S0 = (i * NW + w) * 64;
+      dma16(srdK, kdma[i], stage + S0 * 16);
+      dma16(srdV, vdma[i], stage + KT + S0 * 16);
+    }
+  };
+  int kv_hi = s.sk - 1, kv_lo = -kWinInf;
+  if (BANDED) {
+    kv_hi = min(kv_hi, qi + off_causal + a.win_r);
+    kv_lo = qi + off_causal - a.win_l;
+  }
+  kv_hi -= 4 * h;
+  kv_lo -= 4 * h;
+
+  // Tile n (stage n % 2): S^T, dP^T, dS^T, then dQ += dS K.  Tile n + 1 is
+  // loaded into the other stage at the start of tile n, after the barrier
+  // that ends every wave's reads of tile n - 1.
+  if (n_begin < n_end) prefetch(n_begin);
+  for (int n = n_begin; n < n_end; ++n) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (n + 1 < n_end) prefetch(n + 1);
+    const int sv = svb + (n % NSTAGE) * STAGE;
+    const int ta = tab + (n % NSTAGE) * STAGE, tb = tbb + (n % NSTAGE) * STAGE;
+    f32x16 sc = f32x16{}, pc = f32x16{};
+#pragma unroll
+    for (int sd = 0; sd < NSD; ++sd) {
+      const u32x4 ka = lds_rd128(smem, sv ^ (32 * sd));
+      const u32x4 va = lds_rd128(smem, (sv ^ (32 * sd)) + KT);
+      sc = mfma32<BF16>(ka, qf[sd], sc);
+      pc = mfma32<BF16>(va, df[sd], pc);
+    }
+    const bool masked = (BANDED && (n * BN + BN - 1 > qw + off_causal + a.win_r || n * BN < qw + 31 + off_causal - a.win_l)) ||
+                        (n * BN + BN > s.sk);
+    u32x4 ds[2];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      float t = __builtin_fmaf(sc[j], a.scale_log2, -L2);
+      const int ks = n * BN + 8 * (j >> 2) + (j & 3);
+      if (masked) t = (ks <= kv_hi && ks >= kv_lo) ? t : -__builtin_inff();
+      const float pv = fast_exp2(t);
+      pc[j] = pv * (pc[j] + Dl);  // Dl holds -Delta
+      if (j & 1) ds[j >> 3][(j & 7) >> 1] = pack2<BF16>(pc[j - 1], pc[j]);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int ro = 16 * s2 * RB;
+#pragma unroll
+      for (int t = 0; t < TD; ++t) {
+        const u32x4 kb = tr_frag_b(smem, (ta ^ (64 * t)) + ro, (tb ^ (64 * t)) + ro);
+        dq_acc[t] = mfma32<BF16>(ds[s2], kb, dq_acc[t]);
+      }
+    }
+  }
+
+  {
+    const int rows = min(BM, s.sq - q0);
+    const uint16_t* dqb = a.dq + s.bq * a.dq_b + (int64_t)(s.q0 + q0) * a.dq_r + (int64_t)hq * a.dq_h;
+    const rsrc_t rDQ = make_rsrc(dqb, ((int64_t)(rows - 1) * a.dq_r + hd) * 2);
+#pragma unroll
+    for (int t = 0; t < TD; ++t) {
+      const int d = 32 * t + c32;
+      const bool ok = d < hd;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int qr = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
+        buf_store_u16(rDQ, ok ? (qr * (int)a.dq_r + d) * 2 : kOffOOB, to_bits<BF16>(dq_acc[t][j] * a.scale));
+      }
+    }
+  }
+}
 
 }  // namespace attn

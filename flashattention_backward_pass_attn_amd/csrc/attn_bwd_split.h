@@ -1,26 +1,28 @@
 // Attention backward on gfx950 as two matrix-core kernels that never use
-// atomics: a KV-stationary kernel for dK and dV and a Q-stationary kernel for
-// dQ.  Both recompute P = exp2(S*scale*log2e - LSE*log2e) from the saved LSE
+// atomics: a KV-stationary kernel for dK and dV (this file) and a
+// Q-stationary kernel for dQ (attn_bwd_dq.h).  Both recompute
+// P = exp2(S*scale*log2e - LSE*log2e) from the saved LSE tile by tile
 // (tilelang test_tilelang_kernel_mha_bwd.py, flashattn_bwd) and
-// dS = P o (dP - Delta) with Delta from the preprocess.
+// dS = P o (dP - Delta) with Delta from the preprocess; nothing of size
+// Sq x Sk is ever written to memory.
 //
 // Why two kernels: the pages accumulate dQ across key blocks with fp32
 // atomics (tilelang flashattn_bwd's atomic_add; the CK mha_bwd.cpp page's
-// dq_accum).  On MI355X the device-wide fp32 atomic rate is ~330 G lane-ops/s
-// for every access shape, which for a causal S=4096, d=128 workload puts a
-// floor of ~1.7 ms (128-key blocks) under the dQ accumulation alone.  The
-// Q-stationary dQ kernel recomputes S and dP (two extra GEMMs, 7 instead of 5
-// per tile pair) but keeps dQ in registers, writes it once, and is
-// deterministic by construction (key blocks are summed in ascending order).
+// dq_accum).  On MI355X the device-wide fp32 atomic rate measures about
+// 340 G lane-ops/s for every access shape (bench_calibrate.hip), which for a
+// causal S=4096, d=128 workload puts a floor of about 1.6 ms (128-key blocks)
+// under the dQ accumulation alone.  The Q-stationary dQ kernel recomputes S
+// and dP (two extra GEMMs, 7 instead of 5 per tile pair) but keeps dQ in
+// registers, writes it once, and is deterministic by construction (key
+// blocks are summed in ascending order).
 //
-// The dK/dV kernel (this file; the dQ kernels are in attn_bwd_dq.h) runs 8
-// wave64s, two per SIMD, in two groups half a tile apart, so that on every
-// SIMD one wave's softmax and products share each interval with the other
-// wave's products.  Each wave owns 32 key rows and splits the streamed query
-// tile with a partner wave: the pair computes the two halves of the score
-// tile (no duplicated MFMA work), trades their packed probability/gradient
-// operands through LDS, and then each wave accumulates one half of the head
-// dimension.
+// The dK/dV kernel runs 8 wave64s, two per SIMD, in two groups half a tile
+// apart, so that on every SIMD one wave's softmax and products share each
+// interval with the other wave's products.  Each wave owns 32 key rows and
+// splits the streamed query tile with a partner wave: the pair computes the
+// two halves of the score tile (no duplicated MFMA work), trades their packed
+// probability/gradient operands through LDS, and then each wave accumulates
+// one half of the head dimension.
 #pragma once
 
 #include <type_traits>
@@ -170,7 +172,6 @@ void attn_bwd_dkdv_kernel(Args a) {
     dodma[i] = slot_off(S, (int)a.do_r);
   }
 
-  const int64_t ds_slot = ds_key_slot0(a, z) + (BN / 32) * nb + kvg;  // this wave's 32-key tile in dS^T
   // query tiles that see any key of this block
   int m_begin = 0, m_end = (s.sq + BM - 1) / BM;
   if (BANDED) {
@@ -190,9 +191,6 @@ void attn_bwd_dkdv_kernel(Args a) {
     const uint16_t* qb = a.q + s.bq * a.q_b + (int64_t)s.q0 * a.q_r + (int64_t)hq * a.q_h;
     const uint16_t* db = a.dout + s.bq * a.do_b + (int64_t)s.q0 * a.do_r + (int64_t)hq * a.do_h;
     const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h;
-    // this wave's row of dS^T chunks for query head hq (query tile qt at + qt * 2 KiB)
-    const uint8_t* ds_head = reinterpret_cast<const uint8_t*>(a.ds) +
-                             ((int64_t)hq * a.ds_nkt + ds_slot) * (int64_t)a.ds_nqt * 2048;
 
     // Tile m into stage `st`: Q, dO, LSE, Delta.  Rows past the end read as 0;
     // their P and dS then contribute nothing (Q = dO = 0).  Every wave issues
@@ -224,8 +222,7 @@ void attn_bwd_dkdv_kernel(Args a) {
     };
 
     // Phase 1 of tile m (stage st): S and dP for this wave's 32 queries x 32
-    // keys, P and dS, the packed operands into the exchange slot and dS^T to
-    // the workspace.
+    // keys, P and dS, and the packed operands into the exchange slot.
     auto phase1_body = [&](int m, int st, auto mask) {
       const uint8_t* sQ = smem + st * STAGE;
       // per-tile base (stage offsets leave the chunk bits alone), so the
@@ -329,20 +326,6 @@ void attn_bwd_dkdv_kernel(Args a) {
       *reinterpret_cast<u32x4*>(xown + 1 * 1024) = pf[1];
       *reinterpret_cast<u32x4*>(xown + 2 * 1024) = dsf[0];
       *reinterpret_cast<u32x4*>(xown + 3 * 1024) = dsf[1];
-      // dS^T of this wave's 32 keys x 32 queries for the dQ kernel: lane
-      // (key row c32, half h) writes its 32 bytes -- query runs 4h + 8r
-      // .. +3, r = 0..3 -- at row c32 * 64 + h * 32 of the chunk.
-      {
-        // Without a dS^T workspace (the dQ kernel then recomputes dS), or for
-        // a chunk out of range (a sequence longer than the params say), the
-        // stores are dropped by the descriptor's zero bound -- still issued,
-        // so the memory counter waits below stay exact.
-        const int qt = 2 * m + half;
-        const bool in_range = a.ds != nullptr && qt < a.ds_nqt && ds_slot < a.ds_nkt;
-        const rsrc_t rS = make_rsrc(ds_head + (int64_t)qt * 2048, in_range ? 2048 : 0);
-        buf_store128_nt(rS, c32 * 64 + h * 32, dsf[0]);
-        buf_store128_nt(rS, c32 * 64 + h * 32 + 16, dsf[1]);
-      }
     };
     // Tiles crossing an edge of the band and the partial last key block are
     // masked (zero-filled key rows would otherwise give P = exp(-LSE), which
@@ -414,10 +397,9 @@ void attn_bwd_dkdv_kernel(Args a) {
       // phase 2 of tile j - 1), and this wave's share of tile j + 1 is waited
       // for at the end of interval 2j + 1, before group 0 reads it.
       //
-      // Memory-counter accounting: after tile j + 1's loads a group-0 wave
-      // issues two dS^T stores (phase 1 of tile j) and tile j + 2's loads; a
-      // group-1 wave issues the stores of tile j - 1, tile j + 2's loads and the
-      // stores of tile j.  Two empty stores stand in for tile -1's.
+      // Memory-counter accounting: the loads are the only memory operations
+      // of the loop and complete in issue order, so waiting until at most
+      // NPF are outstanding (the next tile's) means tile j + 1 has landed.
       const int n = m_end - m_begin;
       // The previous head's last interval ended with a barrier: every wave is
       // done with its stages.
@@ -425,14 +407,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       if (first_head) load_kv_lds();
       prefetch(m_begin, 0, true);
       prefetch(m_begin + 1, 1, n > 1);
-      if (grp) {
-        const rsrc_t none = make_rsrc(a.q, 0);
-        buf_store128_nt(none, 0, u32x4{0u, 0u, 0u, 0u});
-        buf_store128_nt(none, 16, u32x4{0u, 0u, 0u, 0u});
-        wait_vmcnt<NPF + 2>();
-      } else {
-        wait_vmcnt<NPF>();
-      }
+      wait_vmcnt<NPF>();
       lds_barrier();  // tile 0 (and K/V) landed
       if (first_head) {
         read_kv_regs();
@@ -443,11 +418,11 @@ void attn_bwd_dkdv_kernel(Args a) {
       for (int j = 0; j < n; ++j) {
         if (grp) prefetch(m_begin + j + 2, st_load, j + 2 < n);
         phase1(m_begin + j, st);
-        if (grp) wait_vmcnt<NPF + 4>();
+        if (grp) wait_vmcnt<NPF>();
         lds_barrier();  // exchange slots written
         if (!grp) prefetch(m_begin + j + 2, st_load, j + 2 < n);
         phase2(st);
-        if (!grp) wait_vmcnt<NPF + 2>();
+        if (!grp) wait_vmcnt<NPF>();
         lds_barrier();  // loads published; stage reads retired
         st = st == 2 ? 0 : st + 1;
         st_load = st_load == 2 ? 0 : st_load + 1;
@@ -475,7 +450,7 @@ void attn_bwd_dkdv_kernel(Args a) {
         phase1(m_begin + j, st);
         lds_barrier();  // exchange slots written
         phase2(st);
-        wait_vmcnt<2>();
+        wait_vmcnt<0>();
         lds_barrier();  // loads published; stage reads retired
         st ^= 1;
       }

@@ -70,22 +70,7 @@ struct Args {
   // (bottom-right aligned).  Causal: win_l = kWinInf, win_r = 0; a local
   // window bounds both sides; kWinInf stands for "no bound".
   int32_t win_l, win_r;
-  // dS^T workspace written by the dK/dV kernel and read by the dQ kernel:
-  // 2 KiB chunks of 32 keys x 32 queries, chunk (head, key tile, query tile)
-  // at ((head * ds_nkt + key tile) * ds_nqt + query tile) * 2048 bytes.
-  uint16_t* ds;
-  int64_t ds_bytes;   // size of that region
-  int64_t ds_nkt;     // key-tile slots per head
-  int32_t ds_nqt;     // query-tile slots per key tile
 };
-
-// Slot of the first 32-key tile of sequence z in the dS^T workspace.  Each
-// sequence gets 4 slots per started 128-key block (its dK/dV workgroups
-// write whole blocks), so consecutive sequences never overlap.
-__device__ inline int64_t ds_key_slot0(const Args& a, int z) {
-  const int64_t kr0 = a.varlen ? (int64_t)a.cu_k[z] : (int64_t)z * a.seqlen_k;
-  return 4 * (kr0 / 128) + 4 * (int64_t)z;
-}
 
 // Per-(sequence) geometry: row offsets into packed tensors and lengths.
 struct Seq {
@@ -276,19 +261,6 @@ __device__ __forceinline__ void buf_store_u16(rsrc_t r, int off, uint16_t v) {
   __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
 
-// 16-byte store, non-temporal (written once, read once much later).
-__device__ __forceinline__ void buf_store128_nt(rsrc_t r, int off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2 /* nt */);
-}
-
-__device__ __forceinline__ void buf_store_f32(rsrc_t r, int off, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
-}
-
-__device__ __forceinline__ void buf_atomic_add_f32(rsrc_t r, int off, float v) {
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, off, 0, 0);
-}
-
 // ---------------------------------------------------------------------------
 // Direct global -> LDS loads (gfx950 buffer_load ... lds).  Lane t's 16 bytes
 // (or 4 bytes) land at LDS byte address m0 + 16*t (4*t); lanes whose offset
@@ -314,12 +286,6 @@ __device__ __forceinline__ u32x4 make_srd(const void* base, int64_t num_bytes) {
 
 __device__ __forceinline__ void dma16(u32x4 srd, int off, uint32_t lds_byte) {
   __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte) : "memory");
-}
-
-// The same, marked non-temporal (data read once: keep it out of the caches'
-// reuse sets).
-__device__ __forceinline__ void dma16_nt(u32x4 srd, int off, uint32_t lds_byte) {
-  __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte) : "memory");
 }
 
 __device__ __forceinline__ void dma4(u32x4 srd, int off, uint32_t lds_byte) {
@@ -351,10 +317,10 @@ __device__ __forceinline__ u32x4 tr_frag_b(const uint8_t* base, int off_a, int o
 
 // Workgroup barrier for LDS hand-off: wait for this wave's LDS reads/writes,
 // then s_barrier.  Unlike __syncthreads() it does not wait for outstanding
-// global memory operations (the dQ atomics stay in flight); a caller that
-// published data with direct global->LDS loads waits for them first with
-// wait_vmcnt<>().  The memory clobber keeps the compiler from moving LDS
-// accesses across it.
+// global memory operations (direct loads of later tiles stay in flight); a
+// caller that published data with direct global->LDS loads waits for them
+// first with wait_vmcnt<>().  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }

@@ -6,8 +6,9 @@
  * saved log-sum-exp instead of storing them, and produces dQ, dK, dV in three
  * launches: a preprocess (Delta = rowsum(dO o O)), a KV-stationary kernel for
  * dK and dV and a Q-stationary kernel for dQ (matrix-core contractions with
- * fp32 accumulation).  The forward produces O and the LSE the backward
- * consumes.
+ * fp32 accumulation).  Nothing of size Sq x Sk is stored: the workspace holds
+ * two fp32 row statistics, O(Sq) per head.  The forward produces O and the
+ * LSE the backward consumes.
  *
  * Conventions for every entry point
  *  - Every tensor pointer is a DEVICE pointer (hipMalloc'd or equivalent) on
@@ -117,30 +118,16 @@ attn_status attn_fwd(const attn_params *p, const void *q, const void *k, const v
                      void *o, float *lse, void *stream);
 
 /*
- * Bytes of device workspace for the fast backward path: Delta, fp32 laid out
- * like lse (the flash-attention CK mha_bwd.cpp page's softmax_d), and
- * LSE * log2(e) in the same layout, each rounded up to 256 bytes, followed by
- * dS = P o (dP - Delta) in the input dtype as
- * 32 x 32 tiles (about 2 * Hq * Sq * Sk bytes, independent of `causal`;
- * varlen: bounded by 2 * Hq * total_k * max_seqlen_q plus padding).  With it
- * the dK/dV kernel, which forms dS anyway, stores it and the dQ kernel is a
- * plain product dQ = scale * dS K over it.  (When one head's dS tiles
- * would span 1 GiB or more -- sequences of roughly 23K keys and up -- the
- * recompute path below is used whatever the workspace; for head_dim above
- * 128, which has no recompute path, attn_bwd then returns
- * ATTN_ERR_UNSUPPORTED.)  Never allocates.
+ * Bytes of device workspace attn_bwd needs: Delta = rowsum(dO o O) (the
+ * flash-attention CK mha_bwd.cpp page's softmax_d) and LSE * log2(e), each
+ * fp32 laid out like lse and rounded up to 256 bytes -- 8 bytes per
+ * (query head, query row), independent of the key length.  The gradient
+ * kernels recompute P and dS tile by tile from LSE and Delta (tilelang
+ * test_tilelang_kernel_mha_bwd.py, flashattn_bwd) and keep dQ in registers,
+ * so nothing else is needed.  Never allocates.
+ * Errors: as attn_fwd's validation; ATTN_ERR_INVALID_ARGUMENT for a NULL bytes.
  */
 attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
-
-/*
- * Bytes of the smallest workspace attn_bwd accepts: the two row statistics
- * only (for head_dim above 128: the full workspace, as above).  With a
- * workspace smaller than attn_bwd_workspace_size() (but at least this), the
- * dQ kernel recomputes S, dP and dS per key tile instead of reading them:
- * more arithmetic, no quadratic memory.  Results are identical in value up
- * to rounding of the same operations and equally deterministic.
- */
-attn_status attn_bwd_workspace_size_min(const attn_params *p, size_t *bytes);
 
 /*
  * Backward: dQ, dK, dV of sum(O o dO).
@@ -153,15 +140,16 @@ attn_status attn_bwd_workspace_size_min(const attn_params *p, size_t *bytes);
  *   dq [.., Sq, H, d], dk, dv [.., Sk, Hk, d]: outputs, fully overwritten; dK
  *   and dV of a KV head are summed over the query heads of its group.
  *   workspace: device buffer, 256-byte aligned, of at least
- *   attn_bwd_workspace_size_min() bytes; attn_bwd_workspace_size() bytes
- *   select the faster path (see there).  Its contents on entry do not matter.
+ *   attn_bwd_workspace_size() bytes, owned by the caller; its contents on
+ *   entry do not matter and it is overwritten.
  *   delta_out: NULL, or a device fp32 buffer laid out like lse that receives
  *   Delta = rowsum(dO o O) (for tests).
  * Three launches on `stream`: the preprocess (Delta), a KV-stationary kernel
- * for dK and dV (which also stores dS with the full workspace), and a
- * Q-stationary kernel for dQ that sums the key blocks in ascending order in
- * registers.  No atomics are used, so every output is bit-identical from run
- * to run; `deterministic` is accepted and always satisfied.
+ * for dK and dV, and a Q-stationary kernel for dQ that recomputes dS and sums
+ * the key blocks in ascending order in registers (dQ * scale and the
+ * conversion are its epilogue: the pages' dQ postprocess, fused).  No atomics
+ * are used, so every output is bit-identical from run to run; `deterministic`
+ * is accepted and always satisfied.
  * Sq == 0 gives dK = dV = 0; Sk == 0 gives dQ = 0.
  * Errors: as attn_fwd, plus ATTN_ERR_WORKSPACE_TOO_SMALL.
  */
@@ -175,11 +163,11 @@ attn_status attn_bwd(const attn_params *p, const void *q, const void *k, const v
  * The same backward pass, launching only the kernels selected in `phases`
  * (bitwise OR of ATTN_PHASE_*): the preprocess, then dK/dV, then dQ.
  * attn_bwd == attn_bwd_phases(..., ATTN_PHASE_ALL).  Lets a caller time or
- * schedule the kernels separately.  The dK/dV and dQ kernels read Delta from
- * `workspace`, which the preprocess writes; with the full workspace the dQ
- * kernel also reads the dS the dK/dV kernel stored there, so the phases must
- * run in this order on one workspace.  A gradient phase whose inputs were not
- * produced that way gives unspecified (but in-bounds) results.  Arguments, validation and errors as
+ * schedule the kernels separately.  The dK/dV and dQ kernels read Delta and
+ * LSE * log2(e) from `workspace`, which the preprocess writes, so the
+ * preprocess must have run on the same workspace first; a gradient phase
+ * whose statistics were not produced that way gives unspecified (but
+ * in-bounds) results.  Arguments, validation and errors as
  * attn_bwd; phases == 0 or an unknown bit is ATTN_ERR_INVALID_ARGUMENT.
  */
 #define ATTN_PHASE_PREPROCESS 1u
@@ -192,10 +180,21 @@ attn_status attn_bwd_phases(const attn_params *p, const void *q, const void *k, 
                             void *workspace, size_t workspace_bytes,
                             float *delta_out, void *stream, unsigned phases);
 
-/* Static, NUL-terminated description of a status code. */
+/*
+ * Static, NUL-terminated description of a status code.  The codes stand in
+ * for the flash-attention CK mha_bwd.cpp page's error reporting: its
+ * TORCH_CHECK argument checks (dtype, contiguity, batch, head_dim, head
+ * counts) become ATTN_ERR_INVALID_ARGUMENT or ATTN_ERR_UNSUPPORTED, and its
+ * negative kernel time ("invalid argument for fmha_bwd") becomes a status
+ * returned before any launch.  Never NULL; unknown codes give
+ * "unknown status".
+ */
 const char *attn_status_string(attn_status s);
 
-/* Library build identifier (static string), e.g. for logs. */
+/*
+ * Library build identifier (static string), e.g. for logs and for matching
+ * committed measurements to a build.  Not from the pages.
+ */
 const char *attn_version(void);
 
 #ifdef __cplusplus

@@ -55,10 +55,8 @@ def make_case(dtype, b, h, hk, sq, sk, d, seed, lengths_q=None, lengths_k=None, 
                                  varlen_lengths_q=lengths_q, varlen_lengths_k=lengths_k)
 
 
-def gpu_run(lib, inp, causal, deterministic=False, scale=None, return_delta=True, minimal_workspace=False,
-            window=(-1, -1)):
-    """Forward then backward on the GPU through the C ABI (fast path, or with
-    ``minimal_workspace`` the path whose dQ kernel recomputes dS)."""
+def gpu_run(lib, inp, causal, deterministic=False, scale=None, return_delta=True, window=(-1, -1)):
+    """Forward then backward on the GPU through the C ABI."""
     import torch
     dt = inp["dtype"]
     q, k, v, do = (upload(inp[n + "_bits"], dt) for n in ("q", "k", "v", "do"))
@@ -72,7 +70,7 @@ def gpu_run(lib, inp, causal, deterministic=False, scale=None, return_delta=True
                   max_seqlen_k=int(inp["lengths_k"].max()) if len(inp["lengths_k"]) else 0)
     o, lse = lib.attn_fwd(q, k, v, causal=causal, softmax_scale=scale, window=window, **kw)
     res = lib.attn_bwd(q, k, v, o, lse, do, causal=causal, softmax_scale=scale, deterministic=deterministic,
-                       return_delta=return_delta, minimal_workspace=minimal_workspace, window=window, **kw)
+                       return_delta=return_delta, window=window, **kw)
     torch.cuda.synchronize()
     out = {"o": o, "lse": lse, "dq": res[0], "dk": res[1], "dv": res[2]}
     if return_delta:

@@ -119,25 +119,49 @@ def test_half_varlen_rejected(clib):
 
 
 def test_workspace_size_and_too_small(clib):
+    """The workspace is the two fp32 row statistics only: 2 * 4 bytes per
+    (query head, query row), each rounded up to 256 bytes, whatever the key
+    length, head dim, mask or deterministic flag."""
     p = _params()
     n = ctypes.c_size_t(0)
-    nmin = ctypes.c_size_t(0)
     assert clib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == fa.ATTN_OK
-    assert clib.attn_bwd_workspace_size_min(ctypes.byref(p), ctypes.byref(nmin)) == fa.ATTN_OK
-    stat = 2 * 8 * 128  # Delta: fp32 [B, H, Sq]
-    assert nmin.value >= stat * 4 and nmin.value % 256 == 0
-    # the full workspace adds the dS tiles: at least Hq * Sq * Sk bf16/fp16 values per sequence
-    assert n.value >= nmin.value + 2 * 8 * 128 * 128 * 2 and n.value % 256 == 0
-    # below the minimum nothing is launched
-    assert _bwd(clib, p, ws_bytes=nmin.value - 1) == fa.ATTN_ERR_WORKSPACE_TOO_SMALL
-    # neither size depends on the deterministic flag (no dQ accumulator)
-    pd = _params(deterministic=1)
-    nd = ctypes.c_size_t(0)
-    assert clib.attn_bwd_workspace_size(ctypes.byref(pd), ctypes.byref(nd)) == fa.ATTN_OK
-    assert nd.value == n.value
+    stat = 2 * 8 * 128 * 4  # fp32 [B, H, Sq]
+    assert n.value == 2 * ((stat + 255) // 256 * 256)
+    # below it nothing is launched
+    assert _bwd(clib, p, ws_bytes=n.value - 1) == fa.ATTN_ERR_WORKSPACE_TOO_SMALL
+    for kw in (dict(deterministic=1), dict(causal=0), dict(seqlen_k=5000), dict(head_dim=256),
+               dict(window_left=10, window_right=3)):
+        q = _params(**kw)
+        m = ctypes.c_size_t(0)
+        assert clib.attn_bwd_workspace_size(ctypes.byref(q), ctypes.byref(m)) == fa.ATTN_OK
+        assert m.value == n.value, kw
     # unaligned workspace
     assert clib.attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
                          n.value, None, None) == fa.ATTN_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_is_linear_in_the_query_length(clib):
+    """O(S) memory at long sequences: B1 H32 S32768 d128 needs 2 * 4 * 32 * 32768
+    bytes (8 MiB), and S65536 twice that -- nothing quadratic."""
+    for s_len in (32768, 65536):
+        p = _params(batch=1, seqlen_q=s_len, seqlen_k=s_len, heads_q=32, heads_kv=32, head_dim=128)
+        for t in ("q", "o", "dout", "dq", "k", "v", "dk", "dv"):
+            setattr(p, t, fa.attn_strides(s_len * 32 * 128, 32 * 128, 128))
+        n = ctypes.c_size_t(0)
+        assert clib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == fa.ATTN_OK
+        assert n.value == 2 * 4 * 32 * s_len
+
+
+def test_varlen_workspace_follows_total_q(clib):
+    p = _params(cu_seqlens_q=FAKE, cu_seqlens_k=FAKE, total_q=1000, total_k=1234)
+    for t in ("q", "o", "dout", "dq"):
+        setattr(p, t, fa.attn_strides(0, 8 * 64, 64))
+    for t in ("k", "v", "dk", "dv"):
+        setattr(p, t, fa.attn_strides(0, 2 * 64, 64))
+    n = ctypes.c_size_t(0)
+    assert clib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == fa.ATTN_OK
+    stat = 8 * 1000 * 4  # fp32 [H, total_q]
+    assert n.value == 2 * ((stat + 255) // 256 * 256)
 
 
 def test_bad_phase_mask_rejected(clib):
@@ -152,17 +176,3 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 8, 2, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa.attn_fwd(q, q, q)
-
-
-def test_wide_head_dim_needs_the_full_workspace(clib):
-    """Head dims above 128 (the 256-wide tile) have only the stored-dS path: the
-    minimum workspace is the full one, and a Delta-only workspace is refused
-    before anything is launched."""
-    for d in (136, 192, 256):
-        p = _params(head_dim=d)
-        n = ctypes.c_size_t(0)
-        nmin = ctypes.c_size_t(0)
-        assert clib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == fa.ATTN_OK
-        assert clib.attn_bwd_workspace_size_min(ctypes.byref(p), ctypes.byref(nmin)) == fa.ATTN_OK
-        assert nmin.value == n.value
-        assert _bwd(clib, p, ws_bytes=n.value - 256) == fa.ATTN_ERR_WORKSPACE_TOO_SMALL

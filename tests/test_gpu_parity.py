@@ -2,10 +2,10 @@
 
 Element-by-element comparison on seeded inputs at sizes the oracle finishes in
 seconds (several tiles, ragged tails, GQA, varlen, causal with Sq != Sk, rows
-that see no key), and at the full workload sizes on sampled heads plus
-properties that hold at any size.  Bar: max|err| <= 2e-2 * max|ref| (fp16) or
-4e-2 * max|ref| (bf16) per output tensor; |LSE err| <= 1e-3; the deterministic
-mode is bit-identical from run to run.
+that see no key), and at the full workload sizes on every (sequence, head),
+in the launch configuration bench.py times.  Bar: max|err| <= 2e-2 * max|ref|
+(fp16) or 4e-2 * max|ref| (bf16) per output tensor; |LSE err| <= 1e-3; the
+deterministic mode is bit-identical from run to run.
 """
 import math
 
@@ -65,19 +65,8 @@ def test_small_parity(lib, case):
     _compare(out, ref, case[1])
 
 
-@pytest.mark.parametrize("case", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
-def test_small_parity_minimal_workspace(lib, case):
-    """The path for a Delta-only workspace: the dQ kernel recomputes dS."""
-    print(f"[gpu] small parity, minimal workspace {case[0]}", flush=True)
-    inp = _inputs(case, seed=4321)
-    causal = case[8]
-    out = gpu_run(lib, inp, causal, minimal_workspace=True)
-    ref = oracle_run(inp, causal)
-    _compare(out, ref, case[1])
-
-
-# Head dims above 128 run the 256-wide tile (dK/dV in one kernel, dQ as two
-# 128-wide halves of the stored-dS product); same layout as SMALL_CASES.
+# Head dims above 128 run the 256-wide tile (the dK/dV kernel at one wave per
+# SIMD, the four-wave dQ kernel with 32-key tiles); same layout as SMALL_CASES.
 WIDE_CASES = [
     ("d256_bf16_causal_ragged", "bf16", 2, 4, 2, 200, 200, 256, True, None),
     ("d192_fp16_noncausal_gqa", "fp16", 1, 8, 2, 257, 190, 192, False, None),
@@ -123,28 +112,14 @@ WINDOW_CASES = [
 ]
 
 
-@pytest.mark.parametrize("minimal", [False, True], ids=["stored_ds", "recompute"])
 @pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
-def test_window_parity(lib, case, minimal):
-    print(f"[gpu] window parity {case[0]} minimal={minimal}", flush=True)
+def test_window_parity(lib, case):
+    print(f"[gpu] window parity {case[0]}", flush=True)
     inp = _inputs(case[:10], seed=2024)
     causal, window = case[8], case[10]
-    out = gpu_run(lib, inp, causal, minimal_workspace=minimal, window=window)
+    out = gpu_run(lib, inp, causal, window=window)
     ref = oracle_run(inp, causal, window=window)
     _compare(out, ref, case[1])
-
-
-def test_both_workspace_paths_agree(lib):
-    """dK, dV identical; dQ within the rounding of the same operations."""
-    print("[gpu] fast vs minimal workspace, ragged causal bf16 d128", flush=True)
-    case = SMALL_CASES[1]
-    inp = _inputs(case, seed=7)
-    a = gpu_run(lib, inp, True)
-    b = gpu_run(lib, inp, True, minimal_workspace=True)
-    for n in ("dk", "dv"):
-        assert np.array_equal(_bits(a[n]), _bits(b[n])), n
-    da, db = to_f64(a["dq"]), to_f64(b["dq"])
-    assert np.max(np.abs(da - db)) <= 1e-2 * np.max(np.abs(db))
 
 
 @pytest.mark.parametrize("case", [SMALL_CASES[1], SMALL_CASES[4], SMALL_CASES[6]], ids=lambda c: c[0])
@@ -179,7 +154,36 @@ def test_workload_mha_fp16_b1_h2_s128_d64(lib):
     _compare(out, ref, w.dtype)
 
 
-def test_workload_mha_causal_fp16_b2_h8_s1024_d64_atomic_and_deterministic(lib):
+def _bits_t(t):
+    return t.contiguous().view(-1).view(__import__("torch").int16)
+
+
+def _repeat_identical(lib, inp, causal, runs, deterministic=True):
+    """Backward `runs` times on the same GPU forward output; every run's dQ,
+    dK, dV must be bit-identical to the first (compared on the GPU)."""
+    import torch
+    dt = inp["dtype"]
+    q, k, v, do = (upload(inp[n + "_bits"], dt) for n in ("q", "k", "v", "do"))
+    kw = {}
+    if "cu_seqlens_q" in inp:
+        kw = dict(cu_seqlens_q=torch.from_numpy(inp["cu_seqlens_q"]).cuda(),
+                  cu_seqlens_k=torch.from_numpy(inp["cu_seqlens_k"]).cuda(),
+                  max_seqlen_q=int(inp["lengths_q"].max()), max_seqlen_k=int(inp["lengths_k"].max()))
+    o, lse = lib.attn_fwd(q, k, v, causal=causal, **kw)
+    first = lib.attn_bwd(q, k, v, o, lse, do, causal=causal, deterministic=deterministic, **kw)
+    for it in range(1, runs):
+        out = lib.attn_bwd(q, k, v, o, lse, do, causal=causal, deterministic=deterministic, **kw)
+        for name, a_, b_ in zip(("dq", "dk", "dv"), first, out):
+            assert torch.equal(_bits_t(a_), _bits_t(b_)), (it, name)
+    torch.cuda.synchronize()
+    return first
+
+
+def test_workload_mha_causal_fp16_b2_h8_s1024_d64_deterministic(lib):
+    """The causal fp16 S1024 workload: parity with the oracle with and without
+    the deterministic flag, and 10 backward runs bit-identical.  dQ never uses
+    atomics here, so the two flag values run the same ordered path and must
+    agree bit for bit too."""
     name = "mha_causal_fp16_b2_h8_s1024_d64"
     print(f"[gpu] workload {name}", flush=True)
     w = workloads.WORKLOADS[name]
@@ -187,19 +191,24 @@ def test_workload_mha_causal_fp16_b2_h8_s1024_d64_atomic_and_deterministic(lib):
     ref = oracle_run(inp, w.causal)
     out = gpu_run(lib, inp, w.causal, deterministic=False)
     _compare(out, ref, w.dtype)
-    first = None
-    for it in range(10):
-        out_d = gpu_run(lib, inp, w.causal, deterministic=True)
-        if first is None:
-            _compare(out_d, ref, w.dtype)
-            first = {n: _bits(out_d[n]) for n in ("dq", "dk", "dv")}
-        else:
-            for n in ("dq", "dk", "dv"):
-                assert np.array_equal(first[n], _bits(out_d[n])), (it, n)
+    out_d = gpu_run(lib, inp, w.causal, deterministic=True)
+    _compare(out_d, ref, w.dtype)
+    for n in ("dq", "dk", "dv"):
+        assert np.array_equal(_bits(out[n]), _bits(out_d[n])), n
+    _repeat_identical(lib, inp, w.causal, 10)
 
 
-def _full_size_sampled(lib, name, samples):
-    """Run the whole workload on the GPU; compare sampled (sequence, KV head) slices to the oracle."""
+def test_workload_mha_causal_bf16_b4_h16_s4096_d128_bit_identical(lib):
+    """The timed workload: 10 backward runs bit-identical."""
+    name = "mha_causal_bf16_b4_h16_s4096_d128"
+    print(f"[gpu] bit identity {name}", flush=True)
+    w = workloads.WORKLOADS[name]
+    _repeat_identical(lib, workloads.make_workload_inputs(name), w.causal, 10)
+
+
+def _full_size(lib, name):
+    """Run the whole workload on the GPU as bench.py launches it; compare every
+    (sequence, KV head group) -- O, LSE, Delta, dQ, dK, dV -- to the oracle."""
     import oracle
     w = workloads.ALL_WORKLOADS[name]
     inp = workloads.make_workload_inputs(name)
@@ -208,76 +217,66 @@ def _full_size_sampled(lib, name, samples):
     G = w.heads_q // w.heads_kv
     tol = TOL[w.dtype]
     res = {n: to_f64(out[n]) for n in ("o", "lse", "dq", "dk", "dv", "delta")}
-    for z, g in samples:
-        heads = list(range(g * G, (g + 1) * G))
+    del out
+    nseq = len(inp["lengths_q"]) if w.varlen else w.batch
+    want = {n: np.zeros_like(res[n]) for n in res}
+    for z in range(nseq):
         if w.varlen:
             cq = inp["cu_seqlens_q"]
-            a, e = int(cq[z]), int(cq[z + 1])
-            sl = slice(a, e)
+            sl = slice(int(cq[z]), int(cq[z + 1]))
             q, k, v, do = (inp[n][None, sl] for n in ("q", "k", "v", "do"))
-            got = {n: res[n][None, sl] for n in ("o", "dq", "dk", "dv")}
-            got["lse"] = res["lse"][None, :, sl]
-            got["delta"] = res["delta"][None, :, sl]
         else:
             q, k, v, do = (inp[n][z:z + 1] for n in ("q", "k", "v", "do"))
-            got = {n: res[n][z:z + 1] for n in ("o", "dq", "dk", "dv")}
-            got["lse"] = res["lse"][z:z + 1]
-            got["delta"] = res["delta"][z:z + 1]
-        o, lse = oracle.attention_forward(q, k, v, scale, w.causal, heads=heads)
-        dq, dk, dv, delta = oracle.attention_backward(q, k, v, do, scale, w.causal, heads=heads)
-        hs = np.array(heads)
-        assert_close("o", got["o"][:, :, hs], o[:, :, hs], tol)
-        assert_lse_close(got["lse"][:, hs], lse[:, hs])
-        assert_close("delta", got["delta"][:, hs], delta[:, hs], tol)
-        assert_close("dq", got["dq"][:, :, hs], dq[:, :, hs], tol)
-        assert_close("dk", got["dk"][:, :, g], dk[:, :, g], tol)
-        assert_close("dv", got["dv"][:, :, g], dv[:, :, g], tol)
-    # properties at any size: sum over keys of dK is ~0; sum over keys of dV = sum of the group's dO
-    dk_all, dv_all = res["dk"], res["dv"]
-    do_all = inp["do"].astype(np.float64)
-    if w.varlen:
-        cq = inp["cu_seqlens_q"]
-        for z in range(len(cq) - 1):
-            sl = slice(int(cq[z]), int(cq[z + 1]))
-            _sum_checks(dk_all[sl][None], dv_all[sl][None], do_all[sl][None], G)
-    else:
-        _sum_checks(dk_all, dv_all, do_all, G)
+        for g in range(w.heads_kv):
+            heads = list(range(g * G, (g + 1) * G))
+            hs = np.array(heads)
+            o, lse = oracle.attention_forward(q, k, v, scale, w.causal, heads=heads)
+            dq, dk, dv, delta = oracle.attention_backward(q, k, v, do, scale, w.causal, heads=heads)
+            if w.varlen:
+                want["o"][sl, hs] = o[0][:, hs]
+                want["dq"][sl, hs] = dq[0][:, hs]
+                want["dk"][sl, g] = dk[0][:, g]
+                want["dv"][sl, g] = dv[0][:, g]
+                want["lse"][hs, sl] = lse[0][hs]
+                want["delta"][hs, sl] = delta[0][hs]
+            else:
+                want["o"][z][:, hs] = o[0][:, hs]
+                want["dq"][z][:, hs] = dq[0][:, hs]
+                want["dk"][z][:, g] = dk[0][:, g]
+                want["dv"][z][:, g] = dv[0][:, g]
+                want["lse"][z][hs] = lse[0][hs]
+                want["delta"][z][hs] = delta[0][hs]
+    errs = {}
+    for n in ("o", "delta", "dq", "dk", "dv"):
+        errs[n] = assert_close(n, res[n], want[n], tol)
+    assert_lse_close(res["lse"], want["lse"])
+    print(f"[gpu] {name}: " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     return res
 
 
-def _sum_checks(dk, dv, do, G):
-    b, sk, hk, d = dk.shape
-    s_dk = dk.sum(axis=1)
-    assert np.abs(s_dk).max() <= 1e-2 * np.abs(dk).sum(axis=1).max() + 1e-6
-    want = do.sum(axis=1).reshape(b, hk, G, d).sum(axis=2)
-    assert np.abs(dv.sum(axis=1) - want).max() <= 2e-2 * max(np.abs(want).max(), 1e-6)
+def test_workload_mha_causal_bf16_b4_h16_s4096_d128_full(lib):
+    print("[gpu] full-size causal bf16 B4 H16 S4096 d128, every head", flush=True)
+    _full_size(lib, "mha_causal_bf16_b4_h16_s4096_d128")
 
 
-def test_measured_shape_causal_bf16_b2_h16_s4096_d256_sampled(lib):
-    """The head-dim-256 shape bench.py measures, at full size in its launch
-    configuration: sampled heads against the oracle plus the sum properties."""
-    print("[gpu] full-size causal bf16 B2 H16 S4096 d256 (sampled heads)", flush=True)
-    _full_size_sampled(lib, "mha_causal_bf16_b2_h16_s4096_d256", [(0, 0), (1, 15)])
+def test_workload_gqa_bf16_b2_hq32_hk8_s4096_d128_full(lib):
+    print("[gpu] full-size GQA bf16 B2 Hq32 Hk8 S4096 d128, every head", flush=True)
+    _full_size(lib, "gqa_bf16_b2_hq32_hk8_s4096_d128")
 
 
-def test_measured_shape_causal_fp16_b4_h16_s4096_d128_sampled(lib):
-    print("[gpu] full-size causal fp16 B4 H16 S4096 d128 (sampled heads)", flush=True)
-    _full_size_sampled(lib, "mha_causal_fp16_b4_h16_s4096_d128", [(2, 7)])
+def test_workload_varlen_causal_fp16_16seq_h16_d96_full(lib):
+    print("[gpu] full-size varlen causal fp16 16 seqs H16 d96, every sequence and head", flush=True)
+    _full_size(lib, "varlen_causal_fp16_16seq_h16_d96")
 
 
-def test_workload_mha_causal_bf16_b4_h16_s4096_d128_sampled(lib):
-    print("[gpu] full-size causal bf16 B4 H16 S4096 d128 (sampled heads)", flush=True)
-    _full_size_sampled(lib, "mha_causal_bf16_b4_h16_s4096_d128", [(0, 0), (3, 15)])
+def test_measured_shape_causal_fp16_b4_h16_s4096_d128_full(lib):
+    print("[gpu] full-size causal fp16 B4 H16 S4096 d128, every head", flush=True)
+    _full_size(lib, "mha_causal_fp16_b4_h16_s4096_d128")
 
 
-def test_workload_gqa_bf16_b2_hq32_hk8_s4096_d128_sampled(lib):
-    print("[gpu] full-size GQA bf16 B2 Hq32 Hk8 S4096 d128 (sampled KV head)", flush=True)
-    _full_size_sampled(lib, "gqa_bf16_b2_hq32_hk8_s4096_d128", [(1, 5)])
-
-
-def test_workload_varlen_causal_fp16_16seq_h16_d96_sampled(lib):
-    print("[gpu] full-size varlen causal fp16 16 seqs H16 d96 (sampled sequences)", flush=True)
-    _full_size_sampled(lib, "varlen_causal_fp16_16seq_h16_d96", [(3, 2), (9, 11)])
+def test_measured_shape_causal_bf16_b2_h16_s4096_d256_full(lib):
+    print("[gpu] full-size causal bf16 B2 H16 S4096 d256, every head", flush=True)
+    _full_size(lib, "mha_causal_bf16_b2_h16_s4096_d256")
 
 
 def test_empty_query_gives_zero_dk_dv(lib):
