@@ -23,8 +23,9 @@ ATTN_ERR_HIP = 4
 ATTN_FP16 = 0
 ATTN_BF16 = 1
 
-EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_phases", "attn_status_string",
-                    "attn_version")
+EXPORTED_SYMBOLS = ("attn_fwd", "attn_bwd_workspace_size", "attn_bwd", "attn_bwd_phases", "attn_bwd_noalloc",
+                    "attn_status_string", "attn_version")
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_NOALLOC_SCRATCH_BYTES in include/attn.h
 PHASE_PREPROCESS = 1
 PHASE_DKDV = 2
 PHASE_DQ = 4
@@ -94,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.attn_bwd_phases.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp,
                                     ctypes.c_uint]
     lib.attn_bwd_phases.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -241,6 +244,34 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optiona
     else:
         st = lib.attn_bwd_phases(*args, phases)
     _check(st, "attn_bwd")
+    if return_delta:
+        return dq, dk, dv, delta
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optional[float] = None,
+                     deterministic: bool = False, cu_seqlens_q=None, cu_seqlens_k=None, max_seqlen_q=None,
+                     max_seqlen_k=None, dq=None, dk=None, dv=None, return_delta: bool = False, window=(-1, -1)):
+    """attn_bwd through the entry point that allocates nothing on the device:
+    its statistics live in the library's static scratch array (see
+    attn_bwd_noalloc in include/attn.h).  The outputs are allocated here only
+    when not given."""
+    torch = _torch()
+    lib = load_library()
+    _check_device(q, k, v, o, lse, dout)
+    varlen = cu_seqlens_q is not None
+    p = make_params(q, k, causal, softmax_scale, deterministic, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                    max_seqlen_k, window)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        setattr(p, name, _strides(t, varlen))
+    delta = torch.empty_like(lse) if return_delta else None
+    st = lib.attn_bwd_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                              _ptr(delta), _stream_ptr(q.device))
+    _check(st, "attn_bwd_noalloc")
     if return_delta:
         return dq, dk, dv, delta
     return dq, dk, dv

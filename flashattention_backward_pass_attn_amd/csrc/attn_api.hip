@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "attn.h"
 #include "attn_bwd.h"
@@ -204,6 +205,33 @@ void launch_grads(const Args& a, int dtile, bool causal, unsigned phases, dim3 g
   }
 }
 
+// ---- the no-allocation entry point's workspace ------------------------------
+// attn_bwd_noalloc keeps Delta and LSE * log2(e) in this file-scope device
+// array instead of a caller-provided workspace.  Every GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` is
+// only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// and kept in scratch_ptr[device].
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (nullptr on a HIP error).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +352,18 @@ attn_status attn_bwd(const attn_params* p, const void* q, const void* k, const v
                      size_t workspace_bytes_given, float* delta_out, void* stream) {
   return attn_bwd_phases(p, q, k, v, o, lse, dout, dq, dk, dv, workspace, workspace_bytes_given, delta_out,
                          stream, ATTN_PHASE_ALL);
+}
+
+attn_status attn_bwd_noalloc(const attn_params* p, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv, float* delta_out,
+                             void* stream) {
+  attn_status st = validate_common(p);
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes(p) > kScratchBytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = scratch_for_current_device();
+  if (ws == nullptr) return ATTN_ERR_HIP;
+  return attn_bwd_phases(p, q, k, v, o, lse, dout, dq, dk, dv, ws, kScratchBytes, delta_out, stream,
+                         ATTN_PHASE_ALL);
 }
 
 }  // extern "C"

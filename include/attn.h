@@ -181,6 +181,29 @@ attn_status attn_bwd_phases(const attn_params *p, const void *q, const void *k, 
                             float *delta_out, void *stream, unsigned phases);
 
 /*
+ * attn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Delta and LSE * log2(e) live in a static device
+ * array of ATTN_NOALLOC_SCRATCH_BYTES inside the library (one copy per GPU,
+ * held until the process ends); the call allocates and frees nothing.  The
+ * array's device address is looked up with hipGetSymbolAddress on the first
+ * call on each device.
+ *   Arguments, outputs and errors as attn_bwd (no workspace, workspace_bytes).
+ *   A problem whose attn_bwd_workspace_size() exceeds the array -- more than
+ *   ATTN_NOALLOC_SCRATCH_BYTES / 8 (query head, query row) pairs, minus
+ *   rounding -- returns ATTN_ERR_WORKSPACE_TOO_SMALL before any launch;
+ *   ATTN_ERR_HIP if the array's address cannot be obtained.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (different streams, or other threads) race on it and must be
+ *   serialised by the caller.  Nothing in the array needs to start at zero
+ *   (the preprocess writes all of it before it is read).
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+attn_status attn_bwd_noalloc(const attn_params *p, const void *q, const void *k, const void *v,
+                             const void *o, const float *lse, const void *dout,
+                             void *dq, void *dk, void *dv, float *delta_out, void *stream);
+
+/*
  * Static, NUL-terminated description of a status code.  The codes stand in
  * for the flash-attention CK mha_bwd.cpp page's error reporting: its
  * TORCH_CHECK argument checks (dtype, contiguity, batch, head_dim, head

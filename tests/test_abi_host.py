@@ -176,3 +176,30 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 8, 2, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa.attn_fwd(q, q, q)
+
+
+def _noalloc(clib, p, ptr=FAKE):
+    return clib.attn_bwd_noalloc(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None, None)
+
+
+def test_noalloc_validates_before_anything_else(clib):
+    """attn_bwd_noalloc checks its arguments like attn_bwd, and refuses a
+    problem whose statistics exceed the static array, before any HIP call."""
+    assert _noalloc(clib, _params(batch=0)) == fa.ATTN_ERR_INVALID_ARGUMENT
+    assert _noalloc(clib, _params(head_dim=60)) == fa.ATTN_ERR_INVALID_ARGUMENT
+    rows = fa.NOALLOC_SCRATCH_BYTES // 8 // 8 + 64  # per head, 8 query heads
+    p = _params(batch=1, seqlen_q=rows, seqlen_k=rows)
+    for t in ("q", "o", "dout", "dq"):
+        setattr(p, t, fa.attn_strides(rows * 8 * 64, 8 * 64, 64))
+    for t in ("k", "v", "dk", "dv"):
+        setattr(p, t, fa.attn_strides(rows * 2 * 64, 2 * 64, 64))
+    n = ctypes.c_size_t(0)
+    assert clib.attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == fa.ATTN_OK
+    assert n.value > fa.NOALLOC_SCRATCH_BYTES
+    assert _noalloc(clib, p) == fa.ATTN_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
