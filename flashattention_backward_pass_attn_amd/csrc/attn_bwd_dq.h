@@ -25,7 +25,7 @@ namespace attn {
 constexpr int kDqWaves = 8;              // waves per dQ workgroup (32 queries each), head dim <= 128
 constexpr int kDqBM = 32 * kDqWaves;     // query rows per dQ workgroup
 constexpr int kDqBN = 64;                // key rows per tile
-constexpr int kDqPD = 6;                 // LDS reads in flight ahead of their MFMAs
+constexpr int kDqPD = 4;                 // LDS reads in flight ahead of their MFMAs
 constexpr int kDqWideBM = 128;           // query rows per dQ workgroup, 256-wide head-dim tile
 
 // Slot layout of one key tile of the dQ kernel and where each softmax
@@ -148,6 +148,11 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   f32x16 dq_acc[TD];
 #pragma unroll
   for (int t = 0; t < TD; ++t) dq_acc[t] = f32x16{};
+  // -Delta of this lane's query in every row: the dP^T products start from
+  // it, so they leave dP^T - Delta and dS needs one multiply per element.
+  f32x16 ndl;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ndl[j] = Dl;
 
   // Per-lane LDS offsets, as XOR bases (the swizzle only permutes the chunk
   // bits, so the offset of head-dim step sd is base ^ 32*sd, of dQ tile t
@@ -239,7 +244,7 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   };
   auto stageM = [&](f32x16& sv, f32x16& pv, u32x4* dsv, auto jc) {
     constexpr int j = decltype(jc)::value;
-    pv[j] = sv[j] * (pv[j] + Dl);  // Dl holds -Delta
+    pv[j] = sv[j] * pv[j];  // pv holds dP - Delta
     // dS as the A operand of dQ = dS K (row = query, k = key): k-slot e of
     // 16-key step s2 is key 16*s2 + 8*(e/4) + 4*h + e%4 of the half.
     if constexpr (j & 1) dsv[j >> 3][(j & 7) >> 1] = pack2<BF16>(pv[j - 1], pv[j]);
@@ -259,7 +264,7 @@ void attn_bwd_dq_recompute_kernel(Args a) {
     const int tap = tab + (n_prev % NSTAGE) * STAGE, tbp = tbb + (n_prev % NSTAGE) * STAGE;
     if constexpr (!DRAIN) {
       sc0 = f32x16{};
-      pc0 = f32x16{};
+      pc0 = ndl;
     }
     u32x4 buf[PD];
     auto rd = [&](auto kc) {  // LDS operand of the k-th active slot
@@ -286,7 +291,7 @@ void attn_bwd_dq_recompute_kernel(Args a) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i == Sch::SC && !DRAIN) {  // half 1 accumulators start here
         sc1 = f32x16{};
-        pc1 = f32x16{};
+        pc1 = ndl;
       }
       if constexpr (Sch::active(i, FIRST, DRAIN)) {
         constexpr int k = Sch::rank(i, FIRST, DRAIN);
@@ -387,22 +392,18 @@ void attn_bwd_dq_recompute_kernel(Args a) {
     run(n_end, std::false_type{}, std::true_type{}, std::false_type{});
   }
 
-  // ---- dQ * scale, converted (round to nearest even).  C layout: lane =
-  // head-dim column, rows = queries 32*w + 8*(j/4) + 4*h + j%4.
+  // ---- dQ * scale, rounded to nearest even: the pages' postprocess, fused.
+  // Stored as 16-byte row chunks through this wave's LDS region once every
+  // wave is past its last K-tile read.
+  if (n_begin < n_end) lds_barrier();
+  wait_vmcnt<0>();
   {
-    const int rows = min(BM, s.sq - q0);
-    const uint16_t* dqb = a.dq + s.bq * a.dq_b + (int64_t)(s.q0 + q0) * a.dq_r + (int64_t)hq * a.dq_h;
-    const rsrc_t rDQ = make_rsrc(dqb, ((int64_t)(rows - 1) * a.dq_r + hd) * 2);
-#pragma unroll
-    for (int t = 0; t < TD; ++t) {
-      const int d = 32 * t + c32;
-      const bool ok = d < hd;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qr = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
-        buf_store_u16(rDQ, ok ? (qr * (int)a.dq_r + d) * 2 : kOffOOB, to_bits<BF16>(dq_acc[t][j] * a.scale));
-      }
-    }
+    constexpr int REG = 32 * TD * 72;
+    static_assert(NW * REG <= NSTAGE * STAGE, "epilogue transpose fits the stages");
+    const int rows_ok = min(BM, s.sq - q0) - 32 * w;
+    const uint16_t* dqb = a.dq + s.bq * a.dq_b + (int64_t)(s.q0 + q0 + 32 * w) * a.dq_r + (int64_t)hq * a.dq_h;
+    const rsrc_t rDQ = make_rsrc(dqb, rows_ok > 0 ? ((int64_t)(rows_ok - 1) * a.dq_r + hd) * 2 : 0);
+    store_tile_rows<BF16, TD>(dq_acc, a.scale, smem + w * REG, rDQ, (int)a.dq_r, rows_ok, hd, lane);
   }
 }
 
@@ -434,7 +435,8 @@ void attn_bwd_dq_wide_kernel(Args a) {
   constexpr int KI = BN * CPR / (64 * NW);    // direct loads per wave per K (or V) tile
   static_assert(KI >= 1 && NSTAGE * STAGE <= 160 * 1024, "tile shape");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
+  constexpr int SMEM = NSTAGE * STAGE > NW * 32 * TD * 72 ? NSTAGE * STAGE : NW * 32 * TD * 72;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   const uint32_t smem_lds = lds_addr(smem);
 
   const int lane = threadIdx.x & 63;
@@ -568,20 +570,17 @@ void attn_bwd_dq_wide_kernel(Args a) {
     }
   }
 
+  // dQ * scale, rounded, as 16-byte row chunks through LDS (every wave is
+  // past its last K-tile read once the barrier below is passed).
+  if (n_begin < n_end) lds_barrier();
+  wait_vmcnt<0>();
   {
-    const int rows = min(BM, s.sq - q0);
-    const uint16_t* dqb = a.dq + s.bq * a.dq_b + (int64_t)(s.q0 + q0) * a.dq_r + (int64_t)hq * a.dq_h;
-    const rsrc_t rDQ = make_rsrc(dqb, ((int64_t)(rows - 1) * a.dq_r + hd) * 2);
-#pragma unroll
-    for (int t = 0; t < TD; ++t) {
-      const int d = 32 * t + c32;
-      const bool ok = d < hd;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int qr = 32 * w + 8 * (j >> 2) + 4 * h + (j & 3);
-        buf_store_u16(rDQ, ok ? (qr * (int)a.dq_r + d) * 2 : kOffOOB, to_bits<BF16>(dq_acc[t][j] * a.scale));
-      }
-    }
+    constexpr int REG = 32 * TD * 72;
+    static_assert(NW * REG <= sizeof(smem), "epilogue transpose fits");
+    const int rows_ok = min(BM, s.sq - q0) - 32 * w;
+    const uint16_t* dqb = a.dq + s.bq * a.dq_b + (int64_t)(s.q0 + q0 + 32 * w) * a.dq_r + (int64_t)hq * a.dq_h;
+    const rsrc_t rDQ = make_rsrc(dqb, rows_ok > 0 ? ((int64_t)(rows_ok - 1) * a.dq_r + hd) * 2 : 0);
+    store_tile_rows<BF16, TD>(dq_acc, a.scale, smem + w * REG, rDQ, (int)a.dq_r, rows_ok, hd, lane);
   }
 }
 

@@ -457,21 +457,24 @@ void attn_bwd_dkdv_kernel(Args a) {
     }
 }
 
-  // ---- Epilogue: dK * scale, dV; convert (round to nearest even) and store.
-  const uint16_t* dkb = a.dk + s.bk * a.dk_b + (int64_t)(s.k0 + kv0) * a.dk_r + (int64_t)g * a.dk_h;
-  const uint16_t* dvb = a.dv + s.bk * a.dv_b + (int64_t)(s.k0 + kv0) * a.dv_r + (int64_t)g * a.dv_h;
-  const rsrc_t rDK = make_rsrc(dkb, ((int64_t)(rows_k - 1) * a.dk_r + hd) * 2);
-  const rsrc_t rDV = make_rsrc(dvb, ((int64_t)(rows_k - 1) * a.dv_r + hd) * 2);
-#pragma unroll
-  for (int t = 0; t < TDH; ++t) {
-    const int d = 32 * (TDH * half + t) + c32;
-    const bool ok = d < hd;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kr = 32 * kvg + 8 * (j >> 2) + 4 * h + (j & 3);
-      buf_store_u16(rDK, ok ? (kr * (int)a.dk_r + d) * 2 : kOffOOB, to_bits<BF16>(dk_acc[t][j] * a.scale));
-      buf_store_u16(rDV, ok ? (kr * (int)a.dv_r + d) * 2 : kOffOOB, to_bits<BF16>(dv_acc[t][j]));
-    }
+  // ---- Epilogue: dK * scale and dV, rounded to nearest even, stored as
+  // 16-byte row chunks through this wave's LDS region (every wave is past
+  // its last stage read -- the loop ended on a barrier -- and the empty
+  // prefetches of the last tiles have landed once vmcnt reaches 0).
+  wait_vmcnt<0>();
+  {
+    constexpr int REG = 2 * 32 * TDH * 72;  // LDS bytes per wave: dK and dV tiles
+    static_assert(NW * REG <= SINK, "epilogue transpose fits the stages");
+    const int col0 = 32 * TDH * half;        // this wave's head-dim half
+    const uint16_t* dkb = a.dk + s.bk * a.dk_b + (int64_t)(s.k0 + kv0 + 32 * kvg) * a.dk_r + (int64_t)g * a.dk_h + col0;
+    const uint16_t* dvb = a.dv + s.bk * a.dv_b + (int64_t)(s.k0 + kv0 + 32 * kvg) * a.dv_r + (int64_t)g * a.dv_h + col0;
+    const int rows_ok = rows_k - 32 * kvg;
+    const int cols_ok = hd - col0;
+    const rsrc_t rDK = make_rsrc(dkb, rows_ok > 0 ? ((int64_t)(rows_ok - 1) * a.dk_r + max(cols_ok, 0)) * 2 : 0);
+    const rsrc_t rDV = make_rsrc(dvb, rows_ok > 0 ? ((int64_t)(rows_ok - 1) * a.dv_r + max(cols_ok, 0)) * 2 : 0);
+    uint8_t* lds = smem + w * REG;
+    store_tile_rows<BF16, TDH>(dk_acc, a.scale, lds, rDK, (int)a.dk_r, rows_ok, cols_ok, lane);
+    store_tile_rows<BF16, TDH>(dv_acc, 1.f, lds + REG / 2, rDV, (int)a.dv_r, rows_ok, cols_ok, lane);
   }
 }
 

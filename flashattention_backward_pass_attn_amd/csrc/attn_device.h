@@ -262,6 +262,53 @@ __device__ __forceinline__ void buf_store_u16(rsrc_t r, int off, uint16_t v) {
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue store of a wave's 32-row x 32*NT-column fp32 tile held in the MFMA
+// C layout (tile t: lane l holds column 32t + l%32 and rows 8(j/4) + 4(l/32) +
+// j%4), as 16-bit values into a row-major global matrix.  The tile passes
+// through this wave's LDS region `lds` (32*NT*72 bytes): written column-major
+// (4 consecutive rows per 8-byte write, columns 72 bytes apart, which spreads
+// the 64 lanes over every bank), then read back with the transpose read so
+// that each lane holds 8 consecutive columns of one row, stored as one
+// 16-byte write.  `dst` covers the matrix from the tile's first row and
+// column (row stride `rs` elements); rows >= rows_ok and columns >= cols_ok
+// (a multiple of 8) are not written.  Values are multiplied by `mul` and
+// rounded to nearest even.
+// ---------------------------------------------------------------------------
+template <bool BF16, int NT>
+__device__ __forceinline__ void store_tile_rows(const f32x16* acc, float mul, uint8_t* lds, rsrc_t dst, int rs,
+                                                int rows_ok, int cols_ok, int lane) {
+  constexpr int CS = 72;  // bytes per stored column (32 rows + 4 elements of padding)
+  const int c32 = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x2 v;
+      v[0] = pack2<BF16>(acc[t][4 * jj] * mul, acc[t][4 * jj + 1] * mul);
+      v[1] = pack2<BF16>(acc[t][4 * jj + 2] * mul, acc[t][4 * jj + 3] * mul);
+      *reinterpret_cast<u32x2*>(lds + (32 * t + c32) * CS + (8 * jj + 4 * h) * 2) = v;
+    }
+  }
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  // 16-lane group g reads 16 rows x 8 columns per step: lane s addresses
+  // column d0 + s/4, rows r0 + 4(s%4) .. +3, and receives row r0 + s,
+  // columns d0 .. d0+3 (then d0+4 .. d0+7 from the second read).
+  const int g = lane >> 4, s = lane & 15;
+#pragma unroll
+  for (int it = 0; it < 2 * NT; ++it) {
+    const int b = 4 * it + g;
+    const int r0 = 16 * (b & 1), d0 = 8 * (b >> 1);
+    const uint8_t* p = lds + (d0 + (s >> 2)) * CS + (r0 + 4 * (s & 3)) * 2;
+    const u32x2 x = lds_tr4(reinterpret_cast<const uint16_t*>(p));
+    const u32x2 y = lds_tr4(reinterpret_cast<const uint16_t*>(p + 4 * CS));
+    const int row = r0 + s;
+    const bool ok = row < rows_ok && d0 < cols_ok;
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{x[0], x[1], y[0], y[1]}, dst,
+                                           ok ? (row * rs + d0) * 2 : kOffOOB, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Direct global -> LDS loads (gfx950 buffer_load ... lds).  Lane t's 16 bytes
 // (or 4 bytes) land at LDS byte address m0 + 16*t (4*t); lanes whose offset
 // is out of range write zeros.  Issued through inline asm so that the
