@@ -143,59 +143,67 @@ attn_status last_hip_status() {
 }
 
 // ---- dispatch helpers ------------------------------------------------------
-template <bool BF16, int D>
+template <bool BF16, int D, int DC>
 void launch_fwd_d(const Args& a, bool causal, dim3 grid, hipStream_t st) {
   if (causal)
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, true>), grid, dim3(64 * attn::fwd_waves(D)), 0, st, a);
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, DC, true>), grid, dim3(64 * attn::fwd_waves(D)), 0, st, a);
   else
-    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, false>), grid, dim3(64 * attn::fwd_waves(D)), 0, st, a);
+    hipLaunchKernelGGL((attn::attn_fwd_kernel<BF16, D, DC, false>), grid, dim3(64 * attn::fwd_waves(D)), 0, st, a);
 }
 
 template <bool BF16>
-void launch_fwd(const Args& a, int dtile, bool causal, dim3 grid, hipStream_t st) {
-  if (dtile == 64)
-    launch_fwd_d<BF16, 64>(a, causal, grid, st);
-  else if (dtile == 128)
-    launch_fwd_d<BF16, 128>(a, causal, grid, st);
+void launch_fwd(const Args& a, int dcomp, bool causal, dim3 grid, hipStream_t st) {
+  if (dcomp == 64)
+    launch_fwd_d<BF16, 64, 64>(a, causal, grid, st);
+  else if (dcomp == 96)
+    launch_fwd_d<BF16, 128, 96>(a, causal, grid, st);
+  else if (dcomp == 128)
+    launch_fwd_d<BF16, 128, 128>(a, causal, grid, st);
   else
-    launch_fwd_d<BF16, 256>(a, causal, grid, st);
+    launch_fwd_d<BF16, 256, 256>(a, causal, grid, st);
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, int DC>
 void launch_dkdv_d(const Args& a, bool causal, dim3 grid_kv, hipStream_t st) {
   const dim3 blk(64 * attn::dkdv_waves(D));
   if (causal)
-    hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, true>), grid_kv, blk, 0, st, a);
+    hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, DC, true>), grid_kv, blk, 0, st, a);
   else
-    hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, false>), grid_kv, blk, 0, st, a);
+    hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, DC, false>), grid_kv, blk, 0, st, a);
 }
 
-template <bool BF16, int D>
+template <bool BF16, int D, int DC>
 void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q, hipStream_t st) {
-  if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, D>(a, causal, grid_kv, st);
+  if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, D, DC>(a, causal, grid_kv, st);
   if (phases & ATTN_PHASE_DQ) {
     const dim3 blk(64 * attn::kDqWaves);
     if (causal)
-      hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, true>), grid_q, blk, 0, st, a);
+      hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, DC, true>), grid_q, blk, 0, st, a);
     else
-      hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, false>), grid_q, blk, 0, st, a);
+      hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, DC, false>), grid_q, blk, 0, st, a);
   }
 }
 
+// Head-dim tiles: stored 64, 128 or 256 wide in LDS (columns past head_dim
+// zero-filled); computed 64, 96, 128 or 256 wide (a 96-wide head -- head dims
+// 72..96 -- does three quarters of the 128-wide tile's products).
 int dtile_for(int head_dim) { return head_dim <= 64 ? 64 : (head_dim <= 128 ? 128 : 256); }
+int dcomp_for(int head_dim) { return head_dim <= 64 ? 64 : (head_dim <= 96 ? 96 : (head_dim <= 128 ? 128 : 256)); }
 
 // Query rows per dQ workgroup for a head-dim tile.
 int dq_rows(int dtile) { return dtile == 256 ? attn::kDqWideBM : attn::kDqBM; }
 
 template <bool BF16>
-void launch_grads(const Args& a, int dtile, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q,
+void launch_grads(const Args& a, int dcomp, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q,
                   hipStream_t st) {
-  if (dtile == 64) {
-    launch_grads_d<BF16, 64>(a, causal, phases, grid_kv, grid_q, st);
-  } else if (dtile == 128) {
-    launch_grads_d<BF16, 128>(a, causal, phases, grid_kv, grid_q, st);
+  if (dcomp == 64) {
+    launch_grads_d<BF16, 64, 64>(a, causal, phases, grid_kv, grid_q, st);
+  } else if (dcomp == 96) {
+    launch_grads_d<BF16, 128, 96>(a, causal, phases, grid_kv, grid_q, st);
+  } else if (dcomp == 128) {
+    launch_grads_d<BF16, 128, 128>(a, causal, phases, grid_kv, grid_q, st);
   } else {
-    if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, 256>(a, causal, grid_kv, st);
+    if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, 256, 256>(a, causal, grid_kv, st);
     if (phases & ATTN_PHASE_DQ) {
       if (causal)
         hipLaunchKernelGGL((attn::attn_bwd_dq_wide_kernel<BF16, true>), grid_q, dim3(256), 0, st, a);
@@ -270,8 +278,9 @@ attn_status attn_fwd(const attn_params* p, const void* q, const void* k, const v
   const int dt = dtile_for(p->head_dim);
   const int bm = attn::fwd_bm(dt);
   dim3 grid(p->heads_q * p->batch, (p->seqlen_q + bm - 1) / bm, 1);
-  if (p->dtype == ATTN_BF16) launch_fwd<true>(a, dt, banded(p), grid, hs);
-  else launch_fwd<false>(a, dt, banded(p), grid, hs);
+  const int dc = dcomp_for(p->head_dim);
+  if (p->dtype == ATTN_BF16) launch_fwd<true>(a, dc, banded(p), grid, hs);
+  else launch_fwd<false>(a, dc, banded(p), grid, hs);
   return last_hip_status();
 }
 
@@ -340,8 +349,9 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
     // blocks of every head start first and one head's blocks share an XCD.
     dim3 grid_kv(p->heads_kv * p->batch, kvblocks > 0 ? kvblocks : 1, 1);
     dim3 grid_q(p->heads_q * p->batch, dqblocks > 0 ? dqblocks : 1, 1);
-    if (bf) launch_grads<true>(a, dt, causal, grad_phases, grid_kv, grid_q, hs);
-    else launch_grads<false>(a, dt, causal, grad_phases, grid_kv, grid_q, hs);
+    const int dc = dcomp_for(p->head_dim);
+    if (bf) launch_grads<true>(a, dc, causal, grad_phases, grid_kv, grid_q, hs);
+    else launch_grads<false>(a, dc, causal, grad_phases, grid_kv, grid_q, hs);
     if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
   }
   return ATTN_OK;

@@ -70,6 +70,8 @@ struct DqSchedule {
 // dQ for head dims up to 128: one workgroup per (query head x sequence,
 // 256-query block), 8 waves (two per SIMD), wave w owning queries 32w .. +32
 // of the block; each wave works every 64-key tile alone as two 32-key halves.
+// K and V tiles are stored D wide in LDS (D = 64 or 128) and the products run
+// DC wide (96 for head dims 72-96).
 //
 // Schedule.  The matrix-core work of one tile is a stream of slots
 //   A: S, dP of half 0      B: dQ of the previous tile's half 1
@@ -80,7 +82,7 @@ struct DqSchedule {
 // tile is still read in B, hence three LDS stages (3 x 32 KiB at D = 128),
 // filled by direct global->LDS loads one tile ahead.
 // ---------------------------------------------------------------------------
-template <bool BF16, int D, bool BANDED>
+template <bool BF16, int D, int DC, bool BANDED>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_bwd_dq_recompute_kernel(Args a) {
   constexpr int NW = 8;
@@ -90,8 +92,9 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   constexpr int KT = BN * RB;                // bytes of a K (or V) tile
   constexpr int STAGE = 2 * KT;
   constexpr int NSTAGE = 3;
-  constexpr int TD = D / 32;                 // head-dim tiles of dQ
-  constexpr int NSD = D / 16;                // k-steps of S^T / dP^T
+  static_assert(DC % 32 == 0 && DC <= D, "compute width: 32-column tiles within the stored tile");
+  constexpr int TD = DC / 32;                // head-dim tiles of dQ
+  constexpr int NSD = DC / 16;               // k-steps of S^T / dP^T
   constexpr int KI = BN * CPR / (64 * NW);   // direct loads per wave per K (or V) tile
   static_assert(TD >= 2 && KI >= 1, "head dim of 64 or 128");
   static_assert(BM == 32 * NW && BN == 64, "32 queries per wave, two 32-key halves");

@@ -20,9 +20,10 @@
 // apart, so that on every SIMD one wave's softmax and products share each
 // interval with the other wave's products.  Each wave owns 32 key rows and
 // splits the streamed query tile with a partner wave: the pair computes the
-// two halves of the score tile (no duplicated MFMA work), trades their packed
-// probability/gradient operands through LDS, and then each wave accumulates
-// one half of the head dimension.
+// two halves of the score tile (no duplicated MFMA work); then one wave of
+// the pair accumulates dV and the other dK, each over the whole head
+// dimension, so each sends its partner only the operand the partner lacks:
+// the dV wave sends its dS^T, the dK wave its P^T.
 #pragma once
 
 #include <type_traits>
@@ -44,33 +45,41 @@ constexpr int dkdv_bn(int d) { return 16 * dkdv_waves(d); }
 // 64 for the 256-wide head-dim tile -- looping over the query blocks (and,
 // for GQA, over the query heads of the KV head).
 //   wave w: key rows 32*(w>>1) .. +32 of the block, shared with its partner
-//   w^1; query half (w&1) of each 64-query tile for S = Q K^T and
-//   dP = dO V^T; head-dim half (w&1) for dV += P^T dO and dK += dS^T Q.
+//   w^1; query half R = w&1 of each 64-query tile for S = Q K^T and
+//   dP = dO V^T; then R = 0 accumulates dV += P^T dO and R = 1 dK += dS^T Q
+//   over all 64 queries and all DC / 32 head-dim tiles.
 //   Waves 0-3 and 4-7 (one of each on every SIMD) run half a tile apart.
+// The head dim is stored in a D-wide LDS tile (D = 64, 128, 256; columns
+// past head_dim are zero) and computed DC wide (a multiple of 32, at most D:
+// 96 for head dims 72-96, so a 96-wide head does three quarters of the
+// 128-wide tile's products).
 // LDS (D = 128): three stages of {Q, dO, LSE*log2(e), -Delta} (3 x 32.5 KiB,
-// swizzled, filled by direct global->LDS loads two tiles ahead) + the P/dS
-// exchange (8 x 4 KiB); the block's K and V pass through the last stage and
-// the exchange slots on their way into registers.
+// swizzled, filled by direct global->LDS loads two tiles ahead) + the P or
+// dS exchange (8 x 2 KiB); the block's K and V pass through the last stage
+// and the bytes after it on their way into registers.
 // ---------------------------------------------------------------------------
-template <bool BF16, int D, bool BANDED>
+template <bool BF16, int D, int DC, bool BANDED>
 __global__ __launch_bounds__(64 * dkdv_waves(D)) __attribute__((amdgpu_waves_per_eu(dkdv_waves(D) / 4, dkdv_waves(D) / 4)))
 void attn_bwd_dkdv_kernel(Args a) {
+  static_assert(DC % 32 == 0 && DC <= D, "compute width: 32-column tiles within the stored tile");
   constexpr int NW = dkdv_waves(D);
   constexpr int BM = kDkvBM, BN = dkdv_bn(D);
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RB = D * 2;                  // bytes per row
   constexpr int TILE = BM * RB;
   constexpr int STAGE = 2 * TILE + 2 * BM * 4;
-  constexpr int TD = D / 32;                 // head-dim tiles
-  constexpr int TDH = TD / 2;                // head-dim tiles per half
+  constexpr int TD = DC / 32;                // head-dim tiles of this wave's dV or dK
   constexpr int QI = BM * CPR / (64 * NW);   // direct loads per wave per Q (or dO) tile
   constexpr int NPF = 2 * QI + 1;            // direct loads per wave per tile (Q, dO, one stat row)
   // stages of {Q, dO, LSE, Delta}: three (loads two tiles ahead) when they
   // fit in LDS, else two (one tile ahead)
   constexpr int NSTAGE = NW == 8 ? 3 : 2;
-  constexpr int XB = 4 * 16 * 64;            // exchange bytes per wave
-  constexpr int SINK = NSTAGE * STAGE + NW * XB;  // 256 bytes the idle waves' stat loads land in
-  static_assert(TDH >= 1 && QI >= 1, "head dim tile of 64, 128 or 256");
+  constexpr int XB = 2 * 16 * 64;            // exchange bytes per wave (two 16-query operands)
+  constexpr int KVR = (NSTAGE - 1) * STAGE;  // LDS byte offset of the K tile, V follows
+  // 256 bytes the idle waves' stat loads land in, past the stages, the
+  // exchange slots and the K/V staging
+  constexpr int SINK = NSTAGE * STAGE + NW * XB > KVR + 2 * BN * RB ? NSTAGE * STAGE + NW * XB : KVR + 2 * BN * RB;
+  static_assert(TD >= 1 && QI >= 1, "head dim tile of 64, 128 or 256");
   static_assert(SINK + 256 <= 160 * 1024, "LDS");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SINK + 256];
@@ -80,7 +89,7 @@ void attn_bwd_dkdv_kernel(Args a) {
   const int lane = tid & 63;
   const int w = wave_id();
   const int kvg = w >> 1;         // key-row group of this wave (a pair of waves)
-  const int half = w & 1;         // query half (S, dP) and head-dim half (dV, dK)
+  const int half = w & 1;         // query half (S, dP); 0 accumulates dV, 1 dK
   const int grp = w >> 2;         // pipeline group: 0 runs half a tile ahead of 1
   const int h = lane >> 5;
   const int c32 = lane & 31;
@@ -105,14 +114,12 @@ void attn_bwd_dkdv_kernel(Args a) {
   // dP = dO V^T (column = key, k = head dim), held in registers for the whole
   // workgroup.  They come through LDS: the block's K and V tiles are loaded
   // with direct global->LDS loads (16 contiguous bytes per lane, each row
-  // once) into the region of the last stage and the exchange slots, which
-  // the loop first touches after the first tile, and each wave then reads its
+  // once) into the region of the last stage and past it, which the loop
+  // first touches after the first tile, and each wave then reads its
   // fragments with conflict-free row reads of the swizzled tiles.  Rows past
   // the end read as 0.
-  u32x4 kf[D / 16], vf[D / 16];
-  constexpr int KVR = (NSTAGE - 1) * STAGE;     // LDS byte offset of the K tile, V follows
+  u32x4 kf[DC / 16], vf[DC / 16];
   constexpr int KVI = BN * CPR / (64 * NW);     // direct loads per wave per K (or V) tile
-  static_assert(KVR + 2 * BN * RB <= SINK, "K/V staging fits the last stage and the exchange slots");
   auto load_kv_lds = [&] {
     const uint16_t* kb = a.k + s.bk * a.k_b + (int64_t)(s.k0 + kv0) * a.k_r + (int64_t)g * a.k_h;
     const uint16_t* vb = a.v + s.bk * a.v_b + (int64_t)(s.k0 + kv0) * a.v_r + (int64_t)g * a.v_h;
@@ -132,27 +139,24 @@ void attn_bwd_dkdv_kernel(Args a) {
   auto read_kv_regs = [&] {
     const int kvo = KVR + tile_off<CPR>(32 * kvg + c32, 8 * h);
 #pragma unroll
-    for (int sd = 0; sd < D / 16; ++sd) {
+    for (int sd = 0; sd < DC / 16; ++sd) {
       kf[sd] = lds_rd128(smem, kvo ^ (32 * sd));
       vf[sd] = lds_rd128(smem, (kvo ^ (32 * sd)) + BN * RB);
     }
   };
 
-  f32x16 dk_acc[TDH], dv_acc[TDH];
+  f32x16 acc[TD];  // dV (half 0) or dK (half 1) of this wave's 32 keys
 #pragma unroll
-  for (int t = 0; t < TDH; ++t) {
-    dk_acc[t] = f32x16{};
-    dv_acc[t] = f32x16{};
-  }
+  for (int t = 0; t < TD; ++t) acc[t] = f32x16{};
 
   // ---- Per-lane LDS byte offsets (swizzle folded in; rows modulo 16).
   // S/dP A operand: row 32*half + c32, columns 16*sd + 8*h.  The swizzle
   // only permutes the chunk bits, so step sd is at svb ^ 32*sd.
   const int svb = 32 * half * RB + tile_off<CPR>(c32, 8 * h);
-  int ta[TDH], tb[TDH];  // dV/dK B operand: rows 4*h + rr (+8), columns of this wave's head-dim tiles
+  int ta[TD], tb[TD];  // dV/dK B operand: rows 4*h + rr (+8), columns 32t + tcol
 #pragma unroll
-  for (int t = 0; t < TDH; ++t) {
-    const int col = 32 * (TDH * half + t) + tcol;
+  for (int t = 0; t < TD; ++t) {
+    const int col = 32 * t + tcol;
     ta[t] = tile_off<CPR>(4 * h + rr, col);
     tb[t] = tile_off<CPR>(4 * h + rr + 8, col);
   }
@@ -181,6 +185,9 @@ void attn_bwd_dkdv_kernel(Args a) {
   }
   const int kv_lane = kv0 + 32 * kvg + c32;  // this lane's key column in S / dP
 
+  // The rest runs for a compile-time role R (the wave's half).
+  auto body = [&](auto role_t) {
+  constexpr int R = decltype(role_t)::value;
   // Packed P^T / dS^T operands of this wave's 32 queries, formed in phase 1
   // of a tile and consumed in its phase 2 (for the second group, across the
   // loop's back edge).
@@ -241,8 +248,8 @@ void attn_bwd_dkdv_kernel(Args a) {
       auto read_stats = [&] {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          Lr[jj] = *reinterpret_cast<const f32x4*>(sL + 32 * half + 8 * jj + 4 * h);
-          const f32x4 nd = *reinterpret_cast<const f32x4*>(sDl + 32 * half + 8 * jj + 4 * h);
+          Lr[jj] = *reinterpret_cast<const f32x4*>(sL + 32 * R + 8 * jj + 4 * h);
+          const f32x4 nd = *reinterpret_cast<const f32x4*>(sDl + 32 * R + 8 * jj + 4 * h);
 #pragma unroll
           for (int r = 0; r < 4; ++r) pacc[4 * jj + r] = nd[r];
         }
@@ -253,7 +260,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       // 32*half + 8*(j/4) + 4*h + j%4.  Element (jj, r) is query q_base + e, e = 8*jj + r.  It is visible iff
       // its key (this lane's) is a real row and e_lo <= e <= e_hi, from
       // i + off - win_l <= key <= i + off + win_r.
-      const int q_base = m * BM + 32 * half + 4 * h;
+      const int q_base = m * BM + 32 * R + 4 * h;
       const int d0 = kv_lane - q_base - off_causal;
       const int e_lo = BANDED ? d0 - a.win_r : -kWinInf;
       const int e_hi = BANDED ? d0 + a.win_l : kWinInf;
@@ -266,8 +273,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       // (matrix-core work only) and fills the gaps.
       f32x16 sacc = f32x16{};
       {
-        constexpr int NS = D / 16, PD = 3;
-        static_assert(16 % NS == 0, "P elements spread evenly over the dP products");
+        constexpr int NS = DC / 16, PD = 3;
         u32x4 fr[PD];
         // operand step i: Q for i < NS (S chain), dO for i >= NS (dP chain)
         auto rd = [&](int i, int slot) {
@@ -297,10 +303,9 @@ void attn_bwd_dkdv_kernel(Args a) {
             if (i == 1) read_stats();
           } else {
             pacc = mfma32<BF16>(op, vf[i - NS], pacc);
-            // 16 / NS elements of P per dP product
-            constexpr int EPP = 16 / NS;
+            // the 16 elements of P spread over the NS dP products
 #pragma unroll
-            for (int e = 0; e < EPP; ++e) p_elem(EPP * (i - NS) + e);
+            for (int e = 16 * (i - NS) / NS; e < 16 * (i - NS + 1) / NS; ++e) p_elem(e);
           }
           sched_fence();
         }
@@ -321,11 +326,10 @@ void attn_bwd_dkdv_kernel(Args a) {
           dsf[s2][e] = pack2<BF16>(pacc[8 * s2 + 2 * e], pacc[8 * s2 + 2 * e + 1]);
         }
       }
-      // For the partner wave (same keys, other query half).
-      *reinterpret_cast<u32x4*>(xown + 0 * 1024) = pf[0];
-      *reinterpret_cast<u32x4*>(xown + 1 * 1024) = pf[1];
-      *reinterpret_cast<u32x4*>(xown + 2 * 1024) = dsf[0];
-      *reinterpret_cast<u32x4*>(xown + 3 * 1024) = dsf[1];
+      // For the partner wave (same keys, other query half): the dV wave needs
+      // the dK wave's P^T, the dK wave the dV wave's dS^T.
+      *reinterpret_cast<u32x4*>(xown + 0 * 1024) = R == 0 ? dsf[0] : pf[0];
+      *reinterpret_cast<u32x4*>(xown + 1 * 1024) = R == 0 ? dsf[1] : pf[1];
     };
     // Tiles crossing an edge of the band and the partial last key block are
     // masked (zero-filled key rows would otherwise give P = exp(-LSE), which
@@ -343,40 +347,35 @@ void attn_bwd_dkdv_kernel(Args a) {
       }
     };
 
-    // Phase 2 of tile m (stage st): dV += P^T dO and dK += dS^T Q over all
-    // 64 queries of the tile, for this wave's head-dim half, with the
-    // partner's operands from the exchange slot (written before the barrier
-    // that ends phase 1).  Step = (query half qh, s2, t).
+    // Phase 2 of tile m (stage st): dV += P^T dO (R = 0) or dK += dS^T Q
+    // (R = 1) over all 64 queries of the tile and every head-dim tile, the
+    // other query half's operand from the partner's exchange slot (written
+    // before the barrier that ends phase 1).  Step = (query step sq, head-dim
+    // tile t), this wave's own query half first.
     auto phase2 = [&](int st) {
-      const uint8_t* sQ = smem + st * STAGE;
-      const uint8_t* sdO = sQ + TILE;
-      u32x4 ppf[2], pdsf[2];
-      ppf[0] = *reinterpret_cast<const u32x4*>(xpar + 0 * 1024);
-      ppf[1] = *reinterpret_cast<const u32x4*>(xpar + 1 * 1024);
-      pdsf[0] = *reinterpret_cast<const u32x4*>(xpar + 2 * 1024);
-      pdsf[1] = *reinterpret_cast<const u32x4*>(xpar + 3 * 1024);
-      constexpr int NS = 4 * TDH, PD = 2;
-      u32x4 fo[PD], fq[PD];
+      const uint8_t* sB = smem + st * STAGE + (R == 0 ? TILE : 0);  // dO for dV, Q for dK
+      u32x4 par[2];
+      par[0] = *reinterpret_cast<const u32x4*>(xpar + 0 * 1024);
+      par[1] = *reinterpret_cast<const u32x4*>(xpar + 1 * 1024);
+      constexpr int NS = 4 * TD, PD = 3;
+      u32x4 fb[PD];
       auto rd = [&](int i, int slot) {
-        const int kstep = i / TDH, t = i % TDH;
-        const int qh = (kstep < 2) ? half : (half ^ 1);
-        const int ro = (32 * qh + 16 * (kstep & 1)) * RB;
-        fo[slot] = tr_frag_b(sdO, ro + ta[t], ro + tb[t]);
-        fq[slot] = tr_frag_b(sQ, ro + ta[t], ro + tb[t]);
+        const int sq = (i / TD + 2 * R) & 3, t = i % TD;
+        const int ro = 16 * sq * RB;
+        fb[slot] = tr_frag_b(sB, ro + ta[t], ro + tb[t]);
       };
       sched_fence();
 #pragma unroll
-      for (int i = 0; i < PD; ++i) rd(i, i);
+      for (int i = 0; i < (PD < NS ? PD : NS); ++i) rd(i, i);
       sched_fence();
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
-        const int kstep = i / TDH, t = i % TDH;
-        const u32x4 bo = fo[i % PD], bq = fq[i % PD];
+        const int sq = (i / TD + 2 * R) & 3, t = i % TD;
+        const u32x4 bb = fb[i % PD];
         if (i + PD < NS) rd(i + PD, i % PD);
-        const u32x4 ap = kstep < 2 ? pf[kstep] : ppf[kstep - 2];
-        const u32x4 ad = kstep < 2 ? dsf[kstep] : pdsf[kstep - 2];
-        dv_acc[t] = mfma32<BF16>(ap, bo, dv_acc[t]);
-        dk_acc[t] = mfma32<BF16>(ad, bq, dk_acc[t]);
+        const u32x4 own = R == 0 ? pf[sq & 1] : dsf[sq & 1];
+        const u32x4 av = (sq >> 1) == R ? own : par[sq & 1];
+        acc[t] = mfma32<BF16>(av, bb, acc[t]);
         sched_fence();
       }
     };
@@ -432,8 +431,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       // One wave per SIMD, one group: phase 1, barrier, phase 2, barrier per
       // tile.  Tile j + 1 is loaded into the other stage at the start of
       // tile j (its stage was last read in phase 2 of tile j - 1) and waited
-      // for at the end of tile j; after its loads a wave issues only tile j's
-      // two dS^T stores.
+      // for at the end of tile j.
       const int n = m_end - m_begin;
       const bool first_head = hq == g * a.group;
       if (first_head) load_kv_lds();
@@ -457,25 +455,25 @@ void attn_bwd_dkdv_kernel(Args a) {
     }
 }
 
-  // ---- Epilogue: dK * scale and dV, rounded to nearest even, stored as
-  // 16-byte row chunks through this wave's LDS region (every wave is past
-  // its last stage read -- the loop ended on a barrier -- and the empty
-  // prefetches of the last tiles have landed once vmcnt reaches 0).
+  // ---- Epilogue: dV (R = 0) or dK * scale (R = 1), rounded to nearest
+  // even, stored as 16-byte row chunks through this wave's LDS region
+  // (every wave is past its last stage read -- the loop ended on a barrier --
+  // and the empty prefetches of the last tiles have landed once vmcnt
+  // reaches 0).
   wait_vmcnt<0>();
   {
-    constexpr int REG = 2 * 32 * TDH * 72;  // LDS bytes per wave: dK and dV tiles
+    constexpr int REG = 32 * TD * 72;  // LDS bytes per wave
     static_assert(NW * REG <= SINK, "epilogue transpose fits the stages");
-    const int col0 = 32 * TDH * half;        // this wave's head-dim half
-    const uint16_t* dkb = a.dk + s.bk * a.dk_b + (int64_t)(s.k0 + kv0 + 32 * kvg) * a.dk_r + (int64_t)g * a.dk_h + col0;
-    const uint16_t* dvb = a.dv + s.bk * a.dv_b + (int64_t)(s.k0 + kv0 + 32 * kvg) * a.dv_r + (int64_t)g * a.dv_h + col0;
+    const int64_t orow = R == 0 ? a.dv_r : a.dk_r;
+    const uint16_t* ob = R == 0 ? a.dv + s.bk * a.dv_b + (int64_t)g * a.dv_h : a.dk + s.bk * a.dk_b + (int64_t)g * a.dk_h;
+    ob += (int64_t)(s.k0 + kv0 + 32 * kvg) * orow;
     const int rows_ok = rows_k - 32 * kvg;
-    const int cols_ok = hd - col0;
-    const rsrc_t rDK = make_rsrc(dkb, rows_ok > 0 ? ((int64_t)(rows_ok - 1) * a.dk_r + max(cols_ok, 0)) * 2 : 0);
-    const rsrc_t rDV = make_rsrc(dvb, rows_ok > 0 ? ((int64_t)(rows_ok - 1) * a.dv_r + max(cols_ok, 0)) * 2 : 0);
-    uint8_t* lds = smem + w * REG;
-    store_tile_rows<BF16, TDH>(dk_acc, a.scale, lds, rDK, (int)a.dk_r, rows_ok, cols_ok, lane);
-    store_tile_rows<BF16, TDH>(dv_acc, 1.f, lds + REG / 2, rDV, (int)a.dv_r, rows_ok, cols_ok, lane);
+    const rsrc_t rO = make_rsrc(ob, rows_ok > 0 ? ((int64_t)(rows_ok - 1) * orow + hd) * 2 : 0);
+    store_tile_rows<BF16, TD>(acc, R == 0 ? 1.f : a.scale, smem + w * REG, rO, (int)orow, rows_ok, hd, lane);
   }
+  };
+  if (half) body(std::integral_constant<int, 1>{});
+  else body(std::integral_constant<int, 0>{});
 }
 
 }  // namespace attn

@@ -39,9 +39,10 @@ constexpr float kFwdRescaleSlack = 8.f;
 // O accumulator in registers) runs one.
 constexpr int fwd_waves_per_simd(int d) { return d > 128 ? 1 : 2; }
 
-template <bool BF16, int D, bool BANDED>
+template <bool BF16, int D, int DC, bool BANDED>
 __global__ __launch_bounds__(64 * fwd_waves(D)) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_simd(D), fwd_waves_per_simd(D))))
 void attn_fwd_kernel(Args a) {
+  static_assert(DC % 32 == 0 && DC <= D, "compute width: 32-column tiles within the stored tile");
   constexpr int NW = fwd_waves(D);
   constexpr int BM = fwd_bm(D), BN = kFwdBN;
   constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -51,7 +52,7 @@ void attn_fwd_kernel(Args a) {
   constexpr int NT = 64 * NW;             // threads
   constexpr int NCH = BN * CPR / NT;      // direct loads per thread per K (or V) block
   constexpr int TK = BN / 32;             // key tiles per block
-  constexpr int TD = D / 32;              // head-dim tiles
+  constexpr int TD = DC / 32;             // head-dim tiles computed
   static_assert(BN * CPR % NT == 0, "tile/thread mismatch");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
@@ -80,11 +81,11 @@ void attn_fwd_kernel(Args a) {
   const bool q_ok = qi < s.sq;
 
   // Q as the B operand of S^T = K Q^T: column qi, k = head dim.
-  u32x4 qf[D / 16];
+  u32x4 qf[DC / 16];
   {
     const uint16_t* qp = a.q + s.bq * a.q_b + (int64_t)(s.q0 + qi) * a.q_r + (int64_t)hq * a.q_h;
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
+    for (int st = 0; st < DC / 16; ++st) {
       const int d0 = 16 * st + 8 * h;
       qf[st] = (q_ok && d0 < hd) ? ldg128(qp + d0) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -163,7 +164,7 @@ void attn_fwd_kernel(Args a) {
     for (int tk = 0; tk < TK; ++tk) {
       sc[tk] = f32x16{};
 #pragma unroll
-      for (int sd = 0; sd < D / 16; ++sd) {
+      for (int sd = 0; sd < DC / 16; ++sd) {
         const u32x4 af = lds_rd128(smem, (sbase + 32 * tk * RB + kvb) ^ (32 * sd));
         sc[tk] = mfma32<BF16>(af, qf[sd], sc[tk]);
       }

@@ -31,6 +31,10 @@ SMALL_CASES = [
     ("d32_fp16_causal", "fp16", 1, 2, 2, 70, 70, 32, True, None),
     ("d8_bf16", "bf16", 2, 1, 1, 33, 45, 8, False, None),
     ("s1_fp16_causal", "fp16", 1, 2, 2, 1, 1, 64, True, None),
+    # head dims 72-96 compute a 96-wide tile inside the 128-wide stored one
+    ("d80_bf16_causal_gqa", "bf16", 2, 4, 2, 190, 190, 80, True, None),
+    ("d72_fp16_noncausal_sq_lt_sk", "fp16", 1, 2, 2, 140, 203, 72, False, None),
+    ("d104_fp16_causal", "fp16", 1, 2, 1, 160, 160, 104, True, None),
 ]
 
 
