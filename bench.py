@@ -49,7 +49,7 @@ HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_backward_pass_attn_amd/csrc/attn_bwd_split.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_bwd_dq.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_device.h"]
-TRAFFIC_FILE = "profiles/bwd_{kernel}_traffic_{workload}.json"
+TRAFFIC_FILE = "profiles/{kernel}_traffic_{workload}.json"
 # Matrix-core work of each gradient kernel, in units of 2*b*h*Sq*Sk*d (halved
 # when causal): dK/dV does S, dP, dV, dK; dQ recomputes S and dP and does dQ.
 # The metric counts the method's 5 contractions (10*b*h*Sq*Sk*d) for the whole
@@ -179,7 +179,7 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, command: str) -
         return 1
     f_factor = COPY_BYTES / (sum(fetch[COPY_KERNEL]) / len(fetch[COPY_KERNEL]) * 1024)
     w_factor = COPY_BYTES / (sum(write[COPY_KERNEL]) / len(write[COPY_KERNEL]) * 1024)
-    for kernel in KERNEL_UNITS:
+    for kernel in [*KERNEL_UNITS, "attn_fwd_kernel"]:
         if kernel not in fetch or kernel not in write:
             log(f"{kernel}: missing from the counter files")
             return 1
@@ -195,7 +195,7 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, command: str) -
             "hbm_write_bytes_per_launch": round(wk * 1024 * w_factor),
         }
         rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
-        short = kernel.replace("attn_bwd_", "").replace("_kernel", "")
+        short = kernel.replace("attn_bwd_", "").replace("attn_", "").replace("_kernel", "")
         out = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload, kernel=short))
         os.makedirs(os.path.dirname(out), exist_ok=True)
         with open(out, "w") as f:
@@ -368,6 +368,8 @@ def main(argv=None):
     forward = {"ms": round(fwd_ms, 4), "tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
                "frac": round(fwd_flops / (fwd_ms * 1e-3) / 1e12 / peak, 4), "flop": fwd_flops,
                "kernel": "attn_fwd_kernel", "bound": "mfma"}
+    fwd_traffic = load_traffic(w.name, "fwd")
+    forward["traffic"] = None if fwd_traffic is None else fwd_traffic["hbm_bytes_per_launch"]
     cpu = None
     if args.cpu_baseline_seconds > 0:
         log("cpu baseline: timing the oracle backward on a bounded sample ...")
