@@ -187,11 +187,30 @@ void attn_fwd_kernel(Args a) {
         }
       }
     }
+    // Row max.  With one wave per SIMD (the 256-wide tile) nothing else
+    // fills the latency of a 32-long dependent chain: a tree of depth 5
+    // (measured 10 % faster there); with two waves the chain is as fast.
     float mx = -INFINITY;
+    if constexpr (NW == 4) {
+      float mt[16];
 #pragma unroll
-    for (int tk = 0; tk < TK; ++tk) {
+      for (int j = 0; j < 16; ++j) {
+        mt[j] = sc[0][j];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[tk][j]);
+        for (int tk = 1; tk < TK; ++tk) mt[j] = fmaxf(mt[j], sc[tk][j]);
+      }
+#pragma unroll
+      for (int wdt = 8; wdt >= 1; wdt /= 2) {
+#pragma unroll
+        for (int j = 0; j < wdt; ++j) mt[j] = fmaxf(mt[j], mt[j + wdt]);
+      }
+      mx = mt[0];
+    } else {
+#pragma unroll
+      for (int tk = 0; tk < TK; ++tk) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sc[tk][j]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
     // Lazy rescaling: the exponent reference m_run moves only when some row
@@ -210,13 +229,35 @@ void attn_fwd_kernel(Args a) {
       m_use = (m_run == -INFINITY) ? 0.f : m_run;
     }
     float ls = 0.f;
+    if constexpr (NW == 4) {
 #pragma unroll
-    for (int tk = 0; tk < TK; ++tk) {
+      for (int tk = 0; tk < TK; ++tk) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[tk][j] = fast_exp2(__builtin_fmaf(sc[tk][j], a.scale_log2, -m_use));
+      }
+      // row sum as a tree, in a fixed order
+      float lt[16];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const float p = fast_exp2(__builtin_fmaf(sc[tk][j], a.scale_log2, -m_use));
-        sc[tk][j] = p;
-        ls += p;
+        lt[j] = sc[0][j];
+#pragma unroll
+        for (int tk = 1; tk < TK; ++tk) lt[j] += sc[tk][j];
+      }
+#pragma unroll
+      for (int wdt = 8; wdt >= 1; wdt /= 2) {
+#pragma unroll
+        for (int j = 0; j < wdt; ++j) lt[j] += lt[j + wdt];
+      }
+      ls = lt[0];
+    } else {
+#pragma unroll
+      for (int tk = 0; tk < TK; ++tk) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float p = fast_exp2(__builtin_fmaf(sc[tk][j], a.scale_log2, -m_use));
+          sc[tk][j] = p;
+          ls += p;
+        }
       }
     }
     ls += __shfl_xor(ls, 32);
