@@ -121,10 +121,11 @@ void attn_bwd_dkdv_kernel(Args a) {
   u32x4 kf[DC / 16], vf[DC / 16];
   constexpr int KVI = BN * CPR / (64 * NW);     // direct loads per wave per K (or V) tile
   auto load_kv_lds = [&] {
-    const uint16_t* kb = a.k + s.bk * a.k_b + (int64_t)(s.k0 + kv0) * a.k_r + (int64_t)g * a.k_h;
-    const uint16_t* vb = a.v + s.bk * a.v_b + (int64_t)(s.k0 + kv0) * a.v_r + (int64_t)g * a.v_h;
-    const u32x4 srdK = make_srd(kb, ((int64_t)(rows_k - 1) * a.k_r + hd) * 2);
-    const u32x4 srdV = make_srd(vb, ((int64_t)(rows_k - 1) * a.v_r + hd) * 2);
+    KArgs& ka = kernel_args();
+    const uint16_t* kb = ka.k + s.bk * ka.k_b + (int64_t)(s.k0 + kv0) * ka.k_r + (int64_t)g * ka.k_h;
+    const uint16_t* vb = ka.v + s.bk * ka.v_b + (int64_t)(s.k0 + kv0) * ka.v_r + (int64_t)g * ka.v_h;
+    const u32x4 srdK = make_srd(kb, ((int64_t)(rows_k - 1) * ka.k_r + hd) * 2);
+    const u32x4 srdV = make_srd(vb, ((int64_t)(rows_k - 1) * ka.v_r + hd) * 2);
 #pragma unroll
     for (int i = 0; i < KVI; ++i) {
       const int S = (i * NW + w) * 64 + lane;
@@ -132,8 +133,8 @@ void attn_bwd_dkdv_kernel(Args a) {
       const int c = (S % CPR) ^ swz<CPR>(r);
       const bool ok = 8 * c < hd;
       const uint32_t dst = smem_lds + KVR + (uint32_t)((i * NW + w) * 64) * 16u;
-      dma16(srdK, ok ? (r * (int)a.k_r + 8 * c) * 2 : kOffOOB, dst);
-      dma16(srdV, ok ? (r * (int)a.v_r + 8 * c) * 2 : kOffOOB, dst + BN * RB);
+      dma16(srdK, ok ? (r * (int)ka.k_r + 8 * c) * 2 : kOffOOB, dst);
+      dma16(srdV, ok ? (r * (int)ka.v_r + 8 * c) * 2 : kOffOOB, dst + BN * RB);
     }
   };
   auto read_kv_regs = [&] {
@@ -153,13 +154,11 @@ void attn_bwd_dkdv_kernel(Args a) {
   // S/dP A operand: row 32*half + c32, columns 16*sd + 8*h.  The swizzle
   // only permutes the chunk bits, so step sd is at svb ^ 32*sd.
   const int svb = 32 * half * RB + tile_off<CPR>(c32, 8 * h);
-  int ta[TD], tb[TD];  // dV/dK B operand: rows 4*h + rr (+8), columns 32t + tcol
-#pragma unroll
-  for (int t = 0; t < TD; ++t) {
-    const int col = 32 * t + tcol;
-    ta[t] = tile_off<CPR>(4 * h + rr, col);
-    tb[t] = tile_off<CPR>(4 * h + rr + 8, col);
-  }
+  // dV/dK B operand: rows 4*h + rr (+8), columns 32t + tcol; the column
+  // tile only changes chunk bits above those of tcol, so tile t is at
+  // ta ^ 64*t (tb ^ 64*t).
+  const int ta = tile_off<CPR>(4 * h + rr, tcol);
+  const int tb = tile_off<CPR>(4 * h + rr + 8, tcol);
   uint8_t* const xown = smem + NSTAGE * STAGE + w * XB + lane * 16;
   const uint8_t* const xpar = smem + NSTAGE * STAGE + (w ^ 1) * XB + lane * 16;
 
@@ -195,8 +194,9 @@ void attn_bwd_dkdv_kernel(Args a) {
 
   for (int hq = g * a.group; hq < (g + 1) * a.group; ++hq) {
     if (m_begin >= m_end) break;
-    const uint16_t* qb = a.q + s.bq * a.q_b + (int64_t)s.q0 * a.q_r + (int64_t)hq * a.q_h;
-    const uint16_t* db = a.dout + s.bq * a.do_b + (int64_t)s.q0 * a.do_r + (int64_t)hq * a.do_h;
+    KArgs& ka = kernel_args();
+    const uint16_t* qb = ka.q + s.bq * ka.q_b + (int64_t)s.q0 * ka.q_r + (int64_t)hq * ka.q_h;
+    const uint16_t* db = ka.dout + s.bq * ka.do_b + (int64_t)s.q0 * ka.do_r + (int64_t)hq * ka.do_h;
     const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h;
 
     // Tile m into stage `st`: Q, dO, LSE, Delta.  Rows past the end read as 0;
@@ -213,7 +213,7 @@ void attn_bwd_dkdv_kernel(Args a) {
     // (checked on the host), so no offset wraps.
     const u32x4 srdQh = make_srd(qb, ((int64_t)(s.sq - 1) * a.q_r + hd) * 2);
     const u32x4 srdOh = make_srd(db, ((int64_t)(s.sq - 1) * a.do_r + hd) * 2);
-    const u32x4 srdSh = make_srd((w == 0 ? a.lse2 : a.delta) + st0, w < 2 ? (int64_t)s.sq * 4 : 0);
+    const u32x4 srdSh = make_srd((w == 0 ? ka.lse2 : ka.delta) + st0, w < 2 ? (int64_t)s.sq * 4 : 0);
     auto prefetch = [&](int m, int st, bool real) {
       const uint32_t stage = smem_lds + st * STAGE;
       const uint32_t tq = real ? (uint32_t)(m * BM) * (uint32_t)a.q_r * 2u : (uint32_t)kOffOOB;
@@ -362,7 +362,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       auto rd = [&](int i, int slot) {
         const int sq = (i / TD + 2 * R) & 3, t = i % TD;
         const int ro = 16 * sq * RB;
-        fb[slot] = tr_frag_b(sB, ro + ta[t], ro + tb[t]);
+        fb[slot] = tr_frag_b(sB, ro + (ta ^ (64 * t)), ro + (tb ^ (64 * t)));
       };
       sched_fence();
 #pragma unroll
@@ -464,12 +464,13 @@ void attn_bwd_dkdv_kernel(Args a) {
   {
     constexpr int REG = 32 * TD * 72;  // LDS bytes per wave
     static_assert(NW * REG <= SINK, "epilogue transpose fits the stages");
-    const int64_t orow = R == 0 ? a.dv_r : a.dk_r;
-    const uint16_t* ob = R == 0 ? a.dv + s.bk * a.dv_b + (int64_t)g * a.dv_h : a.dk + s.bk * a.dk_b + (int64_t)g * a.dk_h;
+    KArgs& ka = kernel_args();
+    const int64_t orow = R == 0 ? ka.dv_r : ka.dk_r;
+    const uint16_t* ob = R == 0 ? ka.dv + s.bk * ka.dv_b + (int64_t)g * ka.dv_h : ka.dk + s.bk * ka.dk_b + (int64_t)g * ka.dk_h;
     ob += (int64_t)(s.k0 + kv0 + 32 * kvg) * orow;
     const int rows_ok = rows_k - 32 * kvg;
     const rsrc_t rO = make_rsrc(ob, rows_ok > 0 ? ((int64_t)(rows_ok - 1) * orow + hd) * 2 : 0);
-    store_tile_rows<BF16, TD>(acc, R == 0 ? 1.f : a.scale, smem + w * REG, rO, (int)orow, rows_ok, hd, lane);
+    store_tile_rows<BF16, TD>(acc, R == 0 ? 1.f : ka.scale, smem + w * REG, rO, (int)orow, rows_ok, hd, lane);
   }
   };
   if (half) body(std::integral_constant<int, 1>{});

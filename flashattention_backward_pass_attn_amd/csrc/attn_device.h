@@ -81,13 +81,31 @@ struct Seq {
   int64_t stat_h;    // head stride in lse/delta
 };
 
-__device__ inline Seq seq_info(const Args& a, int z) {
+// Read-only int32 data (the cu_seqlens arrays, never written while a kernel
+// runs) through the constant address space: scalar loads.
+__device__ __forceinline__ int32_t ld_const_i32(const int32_t* p, int i) {
+  return ((__attribute__((address_space(4))) const int32_t*)p)[i];
+}
+
+// The kernel argument block through the constant address space, re-read at
+// each use (an opaque copy of its address per call): for arguments used only
+// outside a kernel's hot loop, so that they are not held in scalar registers
+// across it.
+typedef __attribute__((address_space(4))) const Args KArgs;
+__device__ __forceinline__ KArgs& kernel_args() {
+  const KArgs* p = (const KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *p;
+}
+
+template <class ArgsT>
+__device__ inline Seq seq_info(const ArgsT& a, int z) {
   Seq s;
   if (a.varlen) {
-    s.q0 = a.cu_q[z];
-    s.k0 = a.cu_k[z];
-    s.sq = a.cu_q[z + 1] - s.q0;
-    s.sk = a.cu_k[z + 1] - s.k0;
+    s.q0 = ld_const_i32(a.cu_q, z);
+    s.k0 = ld_const_i32(a.cu_k, z);
+    s.sq = ld_const_i32(a.cu_q, z + 1) - s.q0;
+    s.sk = ld_const_i32(a.cu_k, z + 1) - s.k0;
     s.bq = 0;
     s.bk = 0;
     s.stat0 = s.q0;
