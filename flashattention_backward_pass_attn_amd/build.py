@@ -15,6 +15,9 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
+# per-kernel register, scratch and LDS use reported by the compiler for the
+# last build (tests/test_build_resources.py checks that no kernel spills)
+RESOURCES_PATH = os.path.join(PKG_DIR, "libattn_resources.txt")
 SOURCES = [os.path.join(CSRC, "attn_api.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("attn_device.h", "attn_fwd.h", "attn_bwd.h", "attn_bwd_split.h",
                                               "attn_bwd_dq.h")] + [os.path.join(ROOT, "include", "attn.h")]
@@ -41,17 +44,23 @@ def hipcc_path() -> str:
 def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH) -> str:
     """Compile libattn.so (always recompiles).  Returns the library path."""
     tmp = out_path + ".tmp"
-    cmd = [hipcc_path(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           *SOURCES, "-o", tmp]
+    cmd = [hipcc_path(), *HIPCC_FLAGS, *(extra_flags or []), "-Rpass-analysis=kernel-resource-usage",
+           "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libattn.so")
-    if verbose and res.stderr.strip():
-        sys.stderr.write(res.stderr)
+    remarks = [ln.split("remark:", 1)[1].split("[-Rpass-analysis")[0].rstrip()
+               for ln in res.stderr.splitlines() if "remark:" in ln and "kernel-resource-usage" in ln]
+    other = [ln for ln in res.stderr.splitlines() if "kernel-resource-usage" not in ln]
+    if verbose and any(ln.strip() for ln in other):
+        sys.stderr.write("\n".join(other) + "\n")
     os.replace(tmp, out_path)
+    if out_path == LIB_PATH:
+        with open(RESOURCES_PATH, "w") as f:
+            f.write("\n".join(remarks) + "\n")
     return out_path
 
 
