@@ -416,18 +416,20 @@ void attn_bwd_dq_recompute_kernel(Args a) {
 // (query head x sequence, 128-query block), 4 waves (one per SIMD), wave w
 // owning queries 32w .. +32.  The lane's Q and dO (its column of S^T) stay in
 // registers as B operands (128 registers), dQ accumulates in 8 head-dim tiles
-// (128 accumulation registers).  Key tiles of 32 keys (K and V, 32 KiB) pass
+// (128 accumulation registers).  Key tiles of 64 keys (K and V, 64 KiB) pass
 // through two LDS stages, loaded one tile ahead by direct global->LDS loads.
-// Per tile: S^T and dP^T (alternating head-dim steps), dS^T on the vector
-// ALU, then dQ += dS K; the compiler interleaves the straight-line body.
-// (A software-pipelined version that ran the previous tile's dQ products
-// under this tile's softmax needed more registers than one wave has and
-// spilled.)
+// Per tile, as two 32-key halves: S^T and dP^T of both halves (alternating
+// head-dim steps), dS^T on the vector ALU, then dQ += dS K; the straight-line
+// body lets the compiler run half 0's softmax under half 1's products and
+// half 1's under half 0's dQ products (with one wave per SIMD nothing else
+// fills those gaps; 32-key tiles left them open).  (A software-pipelined
+// version that ran the previous tile's dQ products under this tile's softmax
+// needed more registers than one wave has and spilled.)
 // ---------------------------------------------------------------------------
 template <bool BF16, bool BANDED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_dq_wide_kernel(Args a) {
-  constexpr int D = 256, NW = 4, BM = 32 * NW, BN = 32;
+  constexpr int D = 256, NW = 4, BM = 32 * NW, BN = 64;
   static_assert(BM == kDqWideBM, "grid rows");
   constexpr int CPR = D / 8, RB = D * 2;
   constexpr int KT = BN * RB;                 // bytes of a K (or V) tile
@@ -542,33 +544,45 @@ void attn_bwd_dq_wide_kernel(Args a) {
     if (n + 1 < n_end) prefetch(n + 1);
     const int sv = svb + (n % NSTAGE) * STAGE;
     const int ta = tab + (n % NSTAGE) * STAGE, tb = tbb + (n % NSTAGE) * STAGE;
-    f32x16 sc = f32x16{}, pc = f32x16{};
-#pragma unroll
-    for (int sd = 0; sd < NSD; ++sd) {
-      const u32x4 ka = lds_rd128(smem, sv ^ (32 * sd));
-      const u32x4 va = lds_rd128(smem, (sv ^ (32 * sd)) + KT);
-      sc = mfma32<BF16>(ka, qf[sd], sc);
-      pc = mfma32<BF16>(va, df[sd], pc);
-    }
     const bool masked = (BANDED && (n * BN + BN - 1 > qw + off_causal + a.win_r || n * BN < qw + 31 + off_causal - a.win_l)) ||
                         (n * BN + BN > s.sk);
-    u32x4 ds[2];
+    f32x16 sc[2], pc[2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      float t = __builtin_fmaf(sc[j], a.scale_log2, -L2);
-      const int ks = n * BN + 8 * (j >> 2) + (j & 3);
-      if (masked) t = (ks <= kv_hi && ks >= kv_lo) ? t : -__builtin_inff();
-      const float pv = fast_exp2(t);
-      pc[j] = pv * (pc[j] + Dl);  // Dl holds -Delta
-      if (j & 1) ds[j >> 3][(j & 7) >> 1] = pack2<BF16>(pc[j - 1], pc[j]);
+    for (int kh = 0; kh < 2; ++kh) {
+      sc[kh] = f32x16{};
+      pc[kh] = f32x16{};
+#pragma unroll
+      for (int sd = 0; sd < NSD; ++sd) {
+        const int o = (sv ^ (32 * sd)) + 32 * kh * RB;
+        const u32x4 ka = lds_rd128(smem, o);
+        const u32x4 va = lds_rd128(smem, o + KT);
+        sc[kh] = mfma32<BF16>(ka, qf[sd], sc[kh]);
+        pc[kh] = mfma32<BF16>(va, df[sd], pc[kh]);
+      }
+    }
+    u32x4 ds[2][2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float t = __builtin_fmaf(sc[kh][j], a.scale_log2, -L2);
+        const int ks = n * BN + 32 * kh + 8 * (j >> 2) + (j & 3);
+        if (masked) t = (ks <= kv_hi && ks >= kv_lo) ? t : -__builtin_inff();
+        const float pv = fast_exp2(t);
+        pc[kh][j] = pv * (pc[kh][j] + Dl);  // Dl holds -Delta
+        if (j & 1) ds[kh][j >> 3][(j & 7) >> 1] = pack2<BF16>(pc[kh][j - 1], pc[kh][j]);
+      }
     }
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int ro = 16 * s2 * RB;
+    for (int kh = 0; kh < 2; ++kh) {
 #pragma unroll
-      for (int t = 0; t < TD; ++t) {
-        const u32x4 kb = tr_frag_b(smem, (ta ^ (64 * t)) + ro, (tb ^ (64 * t)) + ro);
-        dq_acc[t] = mfma32<BF16>(ds[s2], kb, dq_acc[t]);
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int ro = (32 * kh + 16 * s2) * RB;
+#pragma unroll
+        for (int t = 0; t < TD; ++t) {
+          const u32x4 kb = tr_frag_b(smem, (ta ^ (64 * t)) + ro, (tb ^ (64 * t)) + ro);
+          dq_acc[t] = mfma32<BF16>(ds[kh][s2], kb, dq_acc[t]);
+        }
       }
     }
   }
