@@ -48,6 +48,8 @@ MFMA_MEASURED_TFLOPS = {"fp16": 2469.0, "bf16": 2469.0}
 HBM_PEAK_GBS = 8000.0
 KERNEL_SOURCES = ["flashattention_backward_pass_attn_amd/csrc/attn_bwd_split.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_bwd_dq.h",
+                  "flashattention_backward_pass_attn_amd/csrc/attn_bwd.h",
+                  "flashattention_backward_pass_attn_amd/csrc/attn_fwd.h",
                   "flashattention_backward_pass_attn_amd/csrc/attn_device.h"]
 TRAFFIC_FILE = "profiles/{kernel}_traffic_{workload}.json"
 # Matrix-core work of each gradient kernel, in units of 2*b*h*Sq*Sk*d (halved
