@@ -337,3 +337,54 @@ def test_outputs_fully_overwritten(lib):
         assert torch.isfinite(t).all().item()
     ref = oracle_run(inp, True)
     assert_close("dq", to_f64(dq), ref["dq"], TOL["fp16"])
+
+
+def test_strided_layouts_packed_qkv(lib):
+    """Q, K, V as views of one packed [B, S, 3, H, d] tensor, dO with a padded
+    head stride, and dQ, dK, dV written into views of a packed gradient
+    tensor: the kernels follow the strides (row and head strides are
+    multiples of 8 elements, the last dimension contiguous)."""
+    import torch
+    print("[gpu] strided layouts: packed qkv, padded dO, packed gradients", flush=True)
+    b, h, s_len, d = 2, 4, 200, 64
+    inp = make_case("bf16", b, h, h, s_len, s_len, d, seed=4242)
+    q, k, v, do = (upload(inp[n + "_bits"], "bf16") for n in ("q", "k", "v", "do"))
+    qkv = torch.empty(b, s_len, 3, h, d, dtype=q.dtype, device=q.device)
+    qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2] = q, k, v
+    qs, ks, vs = qkv.unbind(2)
+    assert qs.stride(1) == 3 * h * d and not qs.is_contiguous()
+    dop = torch.zeros(b, s_len, h, d + 8, dtype=q.dtype, device=q.device)
+    dop[..., :d] = do
+    dos = dop[..., :d]
+    grads = torch.full((b, s_len, 3, h, d), float("nan"), dtype=q.dtype, device=q.device)
+    dqs, dks, dvs = grads.unbind(2)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = lib.attn_fwd(qs, ks, vs, causal=True, softmax_scale=scale)
+    res = lib.attn_bwd(qs, ks, vs, o, lse, dos, causal=True, softmax_scale=scale, dq=dqs, dk=dks, dv=dvs,
+                       return_delta=True)
+    torch.cuda.synchronize()
+    ref = oracle_run(inp, True)
+    out = {"o": o, "lse": lse, "dq": dqs, "dk": dks, "dv": dvs, "delta": res[3]}
+    _compare(out, ref, "bf16")
+    # the same gradients as the contiguous layout, bit for bit
+    base = gpu_run(lib, inp, True)
+    for name, t in (("dq", dqs), ("dk", dks), ("dv", dvs)):
+        assert np.array_equal(_bits(t), _bits(base[name])), name
+
+
+def test_strided_layouts_packed_kv_gqa(lib):
+    """GQA with K and V as views of one packed [B, S, 2, Hk, d] tensor."""
+    import torch
+    print("[gpu] strided layouts: packed kv, GQA", flush=True)
+    b, h, hk, s_len, d = 1, 8, 2, 190, 128
+    inp = make_case("fp16", b, h, hk, s_len, s_len, d, seed=4243)
+    q, k, v, do = (upload(inp[n + "_bits"], "fp16") for n in ("q", "k", "v", "do"))
+    kv = torch.empty(b, s_len, 2, hk, d, dtype=q.dtype, device=q.device)
+    kv[:, :, 0], kv[:, :, 1] = k, v
+    ks, vs = kv.unbind(2)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = lib.attn_fwd(q, ks, vs, causal=False, softmax_scale=scale)
+    dq, dk, dv, delta = lib.attn_bwd(q, ks, vs, o, lse, do, causal=False, softmax_scale=scale, return_delta=True)
+    torch.cuda.synchronize()
+    ref = oracle_run(inp, False)
+    _compare({"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": delta}, ref, "fp16")
