@@ -296,24 +296,22 @@ def main(argv=None):
     ms_wall = (t1 - t0) * 1e3 / K
     log(f"{w.name}: step median {ms_per_step:.4f} ms, mean {ms_mean:.4f} ms, wall {ms_wall:.4f} ms per call")
 
-    # Per-kernel durations: the same backward launched phase by phase, with
+    # Per-kernel durations: the same backward launched phase by phase (the dQ
+    # kernel, which also runs the preprocess for its rows, then dK/dV), with
     # events between the launches (medians over as many steps).
     P = max(1, min(K, 50))
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(P)]
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(P)]
     for i in range(P):
         e = pev[i]
         e[0].record()
-        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_PREPROCESS, **common)
+        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_DQ, **common)
         e[1].record()
         fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_DKDV, **common)
         e[2].record()
-        fa.attn_bwd(q, k, v, o, lse, do, phases=fa.PHASE_DQ, **common)
-        e[3].record()
     torch.cuda.synchronize()
-    pre_ms = med([e[0].elapsed_time(e[1]) for e in pev])
+    dq_ms = med([e[0].elapsed_time(e[1]) for e in pev])
     dkdv_ms = med([e[1].elapsed_time(e[2]) for e in pev])
-    dq_ms = med([e[2].elapsed_time(e[3]) for e in pev])
-    log(f"{w.name}: kernels pre {pre_ms:.4f} dkdv {dkdv_ms:.4f} dq {dq_ms:.4f} ms")
+    log(f"{w.name}: kernels dq (with the preprocess) {dq_ms:.4f} dkdv {dkdv_ms:.4f} ms")
 
     # The forward that supplies O and LSE (not part of the metric).
     fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
@@ -345,12 +343,7 @@ def main(argv=None):
                             "frac": round(kfl / (ms * 1e-3) / 1e12 / peak, 4), "flop": kfl, "bound": "mfma",
                             "contractions": KERNEL_UNITS[name]}
     per_kernel["attn_bwd_dq_kernel"]["symbol"] = DQ_SYMBOL[w.head_dim > 128]
-    # preprocess: reads O and dO (2*d*2 bytes per row) and LSE, writes -Delta
-    # and LSE*log2(e): 4d + 12 bytes per (query head, row)
-    rows = (int(inp["lengths_q"].sum()) if w.varlen else w.batch * w.seqlen) * w.heads_q
-    pre_bytes = rows * (4 * w.head_dim + 12)
-    per_kernel["attn_bwd_pre_kernel"] = {"ms": round(pre_ms, 4), "bound": "hbm", "bytes": pre_bytes,
-                                         "gbs": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1)}
+    per_kernel["attn_bwd_dq_kernel"]["includes"] = "the preprocess of its rows (Delta, LSE*log2(e))"
     dom = max(kernels, key=kernels.get)
     traffic = load_traffic(w.name, dom.replace("attn_bwd_", "").replace("_kernel", ""))
     roofline = {

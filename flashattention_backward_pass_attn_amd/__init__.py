@@ -216,8 +216,10 @@ def attn_bwd(q, k, v, o, lse, dout, causal: bool = False, softmax_scale: Optiona
              phases: int = PHASE_ALL, window=(-1, -1)):
     """dQ, dK, dV (and optionally Delta) of sum(O * dO) for attention.
 
-    ``phases`` selects which of the three kernels to launch (see attn_bwd_phases
-    in include/attn.h); the default launches all of them.  Without a
+    ``phases`` selects the kernels to launch: the dQ kernel (which also runs
+    the preprocess for its rows), the dK/dV kernel, and the standalone
+    preprocess, which runs only without the dQ phase (see attn_bwd_phases in
+    include/attn.h); the default launches dQ, then dK/dV.  Without a
     ``workspace`` one of ``bwd_workspace_size()`` bytes is allocated (two fp32
     row statistics per query row and head).
     """

@@ -172,9 +172,10 @@ void launch_dkdv_d(const Args& a, bool causal, dim3 grid_kv, hipStream_t st) {
     hipLaunchKernelGGL((attn::attn_bwd_dkdv_kernel<BF16, D, DC, false>), grid_kv, blk, 0, st, a);
 }
 
+// dQ first: the dQ kernel also writes the workspace rows (-Delta and
+// LSE * log2(e)) that the dK/dV kernel reads.
 template <bool BF16, int D, int DC>
 void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, dim3 grid_q, hipStream_t st) {
-  if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, D, DC>(a, causal, grid_kv, st);
   if (phases & ATTN_PHASE_DQ) {
     const dim3 blk(64 * attn::kDqWaves);
     if (causal)
@@ -182,6 +183,7 @@ void launch_grads_d(const Args& a, bool causal, unsigned phases, dim3 grid_kv, d
     else
       hipLaunchKernelGGL((attn::attn_bwd_dq_recompute_kernel<BF16, D, DC, false>), grid_q, blk, 0, st, a);
   }
+  if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, D, DC>(a, causal, grid_kv, st);
 }
 
 // Head-dim tiles: stored 64, 128 or 256 wide in LDS (columns past head_dim
@@ -203,13 +205,13 @@ void launch_grads(const Args& a, int dcomp, bool causal, unsigned phases, dim3 g
   } else if (dcomp == 128) {
     launch_grads_d<BF16, 128, 128>(a, causal, phases, grid_kv, grid_q, st);
   } else {
-    if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, 256, 256>(a, causal, grid_kv, st);
     if (phases & ATTN_PHASE_DQ) {
       if (causal)
         hipLaunchKernelGGL((attn::attn_bwd_dq_wide_kernel<BF16, true>), grid_q, dim3(256), 0, st, a);
       else
         hipLaunchKernelGGL((attn::attn_bwd_dq_wide_kernel<BF16, false>), grid_q, dim3(256), 0, st, a);
     }
+    if (phases & ATTN_PHASE_DKDV) launch_dkdv_d<BF16, 256, 256>(a, causal, grid_kv, st);
   }
 }
 
@@ -331,19 +333,21 @@ attn_status attn_bwd_phases(const attn_params* p, const void* q, const void* k, 
   const bool causal = banded(p);  // causal or local window: the banded kernels
   const int dt = dtile_for(p->head_dim);
   const int qblocks = (p->seqlen_q + attn::kPreRows - 1) / attn::kPreRows;
-
-  if ((phases & ATTN_PHASE_PREPROCESS) && qblocks > 0) {
-    dim3 grid(qblocks, p->heads_q, p->batch);
-    if (bf) hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<true>), grid, dim3(256), 0, hs, a);
-    else hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<false>), grid, dim3(256), 0, hs, a);
-    if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
-  }
   unsigned grad_phases = phases & (ATTN_PHASE_DKDV | ATTN_PHASE_DQ);
   const int kvbn = attn::dkdv_bn(dt);
   const int kvblocks = (p->seqlen_k + kvbn - 1) / kvbn;
   const int dqblocks = (p->seqlen_q + dq_rows(dt) - 1) / dq_rows(dt);
   if (kvblocks == 0) grad_phases &= ~ATTN_PHASE_DKDV;  // no keys: nothing to write in dK/dV
   if (dqblocks == 0) grad_phases &= ~ATTN_PHASE_DQ;    // no queries: no dQ rows
+
+  // The dQ kernel runs the preprocess for its own rows; the standalone
+  // preprocess is only needed when the dQ phase does not run.
+  if ((phases & ATTN_PHASE_PREPROCESS) && !(grad_phases & ATTN_PHASE_DQ) && qblocks > 0) {
+    dim3 grid(qblocks, p->heads_q, p->batch);
+    if (bf) hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<true>), grid, dim3(256), 0, hs, a);
+    else hipLaunchKernelGGL((attn::attn_bwd_pre_kernel<false>), grid, dim3(256), 0, hs, a);
+    if (last_hip_status() != ATTN_OK) return ATTN_ERR_HIP;
+  }
   if (grad_phases) {
     // (head x sequence, block): block index slowest, so the longest causal
     // blocks of every head start first and one head's blocks share an XCD.

@@ -1,4 +1,5 @@
-// Attention backward on gfx950: the preprocess.
+// Attention backward on gfx950: the preprocess, standalone and as the part of
+// it that the dQ kernels run themselves.
 //
 // Delta_i = sum_d O_id dO_id, in fp32 (tilelang test_tilelang_kernel_mha_bwd.py,
 // flashattn_bwd_preprocess; the flash-attention CK mha_bwd.cpp page's
@@ -55,6 +56,40 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(Args a) {
       // the exp2-domain LSE the dK/dV kernel stages with Delta
       a.lse2[st0 + r] = a.lse_in[st0 + r] * kLog2e;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The preprocess fused into the dQ kernels.  A dQ wave holds each of its query
+// rows of O and dO as B-operand fragments split over a lane pair: lane c32
+// holds the 8-element chunks 16*sd .. +8 and lane c32 + 32 the chunks
+// 16*sd + 8 .. +8.  Each lane sums O o dO over its chunks in fp32 and the pair
+// adds the two halves, so both lanes end with Delta of the row.
+// ---------------------------------------------------------------------------
+template <bool BF16, int N>
+__device__ __forceinline__ float row_delta_pair(const u32x4 (&o)[N], const u32x4 (&d)[N]) {
+  float acc = 0.f;
+#pragma unroll
+  for (int sd = 0; sd < N; ++sd) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc += from_bits<BF16>((uint16_t)(o[sd][i] & 0xffffu)) * from_bits<BF16>((uint16_t)(d[sd][i] & 0xffffu));
+      acc += from_bits<BF16>((uint16_t)(o[sd][i] >> 16)) * from_bits<BF16>((uint16_t)(d[sd][i] >> 16));
+    }
+  }
+  return acc + __shfl_xor(acc, 32);
+}
+
+// The workspace entries of one query row, written by lane half 0 of its pair:
+// -Delta (the gradient kernels' dP start value) and LSE * log2(e); lane half 1
+// writes Delta to delta_out when the caller asked for it.
+__device__ __forceinline__ void store_row_stats(float* delta, float* lse2_ws, float* delta_out, int64_t idx, int h,
+                                                float lse2, float neg_delta) {
+  if (h == 0) {
+    delta[idx] = neg_delta;
+    lse2_ws[idx] = lse2;
+  } else if (delta_out) {
+    delta_out[idx] = -neg_delta;
   }
 }
 

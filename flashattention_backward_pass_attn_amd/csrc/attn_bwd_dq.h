@@ -127,14 +127,18 @@ void attn_bwd_dq_recompute_kernel(Args a) {
 
   // ---- Q and dO of this lane's query as B operands (k = head dim); LSE and
   // Delta of that query.  Rows past the end read as 0.
-  u32x4 qf[NSD], df[NSD];
+  // O of the same rows and chunks: the preprocess's input (below).
+  u32x4 qf[NSD], df[NSD], of[NSD];
   float L2, Dl;
+  int64_t stat_row;  // workspace index of this lane's row, -1 past the end
   {
     const int rows = min(BM, s.sq - q0);
     const uint16_t* qb = a.q + s.bq * a.q_b + (int64_t)(s.q0 + q0) * a.q_r + (int64_t)hq * a.q_h;
     const uint16_t* db = a.dout + s.bq * a.do_b + (int64_t)(s.q0 + q0) * a.do_r + (int64_t)hq * a.do_h;
+    const uint16_t* ob = a.o + s.bq * a.o_b + (int64_t)(s.q0 + q0) * a.o_r + (int64_t)hq * a.o_h;
     const rsrc_t rQ = make_rsrc(qb, ((int64_t)(rows - 1) * a.q_r + hd) * 2);
     const rsrc_t rO = make_rsrc(db, ((int64_t)(rows - 1) * a.do_r + hd) * 2);
+    const rsrc_t rOut = make_rsrc(ob, ((int64_t)(rows - 1) * a.o_r + hd) * 2);
     const int row = 32 * w + c32;
 #pragma unroll
     for (int sd = 0; sd < NSD; ++sd) {
@@ -142,20 +146,17 @@ void attn_bwd_dq_recompute_kernel(Args a) {
       const bool ok = d0 < hd;
       qf[sd] = buf_load128(rQ, ok ? (row * (int)a.q_r + d0) * 2 : kOffOOB);
       df[sd] = buf_load128(rO, ok ? (row * (int)a.do_r + d0) * 2 : kOffOOB);
+      of[sd] = buf_load128(rOut, ok ? (row * (int)a.o_r + d0) * 2 : kOffOOB);
     }
     const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h + q0;
     L2 = buf_load_f32(make_rsrc(a.lse_in + st0, (int64_t)rows * 4), row * 4) * kLog2e;
-    Dl = buf_load_f32(make_rsrc(a.delta + st0, (int64_t)rows * 4), row * 4);
+    stat_row = row < rows ? st0 + row : -1;
   }
 
   f32x16 dq_acc[TD];
 #pragma unroll
   for (int t = 0; t < TD; ++t) dq_acc[t] = f32x16{};
-  // -Delta of this lane's query in every row: the dP^T products start from
-  // it, so they leave dP^T - Delta and dS needs one multiply per element.
-  f32x16 ndl;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) ndl[j] = Dl;
+  f32x16 ndl;  // -Delta of this lane's query in every row (set below)
 
   // Per-lane LDS offsets, as XOR bases (the swizzle only permutes the chunk
   // bits, so the offset of head-dim step sd is base ^ 32*sd, of dQ tile t
@@ -353,8 +354,16 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   // their own, so the matrix-core accumulators flow through straight loops
   // rather than branches.  A wave runs every tile of the block (tiles it
   // cannot see add exact zeros), so every wave takes the same barriers.
+  if (n_begin < n_end) prefetch(n_begin);
+  // The preprocess for this wave's rows, under the first tile's loads:
+  // -Delta from O and dO, and the workspace rows that the dK/dV kernel
+  // stages.  -Delta goes into every row of ndl: the dP^T products start from
+  // it, so they leave dP^T - Delta and dS needs one multiply per element.
+  Dl = -row_delta_pair<BF16>(of, df);
+  if (stat_row >= 0) store_row_stats(a.delta, a.lse2, a.delta_out, stat_row, h, L2, Dl);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) ndl[j] = Dl;
   if (n_begin < n_end) {
-    prefetch(n_begin);
     wait_vmcnt<0>();
     lds_barrier();
     if (n_begin + 1 < n_end) prefetch(n_begin + 1);
@@ -464,14 +473,18 @@ void attn_bwd_dq_wide_kernel(Args a) {
   const int qw = q0 + 32 * w;
   const int qi = qw + c32;
 
-  u32x4 qf[NSD], df[NSD];
+  // O of the same rows and chunks: the preprocess's input (below).
+  u32x4 qf[NSD], df[NSD], of[NSD];
   float L2, Dl;
+  int64_t stat_row;  // workspace index of this lane's row, -1 past the end
   {
     const int rows = min(BM, s.sq - q0);
     const uint16_t* qb = a.q + s.bq * a.q_b + (int64_t)(s.q0 + q0) * a.q_r + (int64_t)hq * a.q_h;
     const uint16_t* db = a.dout + s.bq * a.do_b + (int64_t)(s.q0 + q0) * a.do_r + (int64_t)hq * a.do_h;
+    const uint16_t* ob = a.o + s.bq * a.o_b + (int64_t)(s.q0 + q0) * a.o_r + (int64_t)hq * a.o_h;
     const rsrc_t rQ = make_rsrc(qb, ((int64_t)(rows - 1) * a.q_r + hd) * 2);
     const rsrc_t rO = make_rsrc(db, ((int64_t)(rows - 1) * a.do_r + hd) * 2);
+    const rsrc_t rOut = make_rsrc(ob, ((int64_t)(rows - 1) * a.o_r + hd) * 2);
     const int row = 32 * w + c32;
 #pragma unroll
     for (int sd = 0; sd < NSD; ++sd) {
@@ -479,10 +492,11 @@ void attn_bwd_dq_wide_kernel(Args a) {
       const bool ok = d0 < hd;
       qf[sd] = buf_load128(rQ, ok ? (row * (int)a.q_r + d0) * 2 : kOffOOB);
       df[sd] = buf_load128(rO, ok ? (row * (int)a.do_r + d0) * 2 : kOffOOB);
+      of[sd] = buf_load128(rOut, ok ? (row * (int)a.o_r + d0) * 2 : kOffOOB);
     }
     const int64_t st0 = s.stat0 + (int64_t)hq * s.stat_h + q0;
-    L2 = buf_load_f32(make_rsrc(a.lse2 + st0, (int64_t)rows * 4), row * 4);
-    Dl = buf_load_f32(make_rsrc(a.delta + st0, (int64_t)rows * 4), row * 4);  // -Delta
+    L2 = buf_load_f32(make_rsrc(a.lse_in + st0, (int64_t)rows * 4), row * 4) * kLog2e;
+    stat_row = row < rows ? st0 + row : -1;
   }
 
   f32x16 dq_acc[TD];
@@ -538,6 +552,9 @@ void attn_bwd_dq_wide_kernel(Args a) {
   // loaded into the other stage at the start of tile n, after the barrier
   // that ends every wave's reads of tile n - 1.
   if (n_begin < n_end) prefetch(n_begin);
+  // the preprocess for this wave's rows, under the first tile's loads
+  Dl = -row_delta_pair<BF16>(of, df);
+  if (stat_row >= 0) store_row_stats(a.delta, a.lse2, a.delta_out, stat_row, h, L2, Dl);
   for (int n = n_begin; n < n_end; ++n) {
     wait_vmcnt<0>();
     lds_barrier();

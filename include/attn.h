@@ -144,10 +144,12 @@ attn_status attn_bwd_workspace_size(const attn_params *p, size_t *bytes);
  *   entry do not matter and it is overwritten.
  *   delta_out: NULL, or a device fp32 buffer laid out like lse that receives
  *   Delta = rowsum(dO o O) (for tests).
- * Three launches on `stream`: the preprocess (Delta), a KV-stationary kernel
- * for dK and dV, and a Q-stationary kernel for dQ that recomputes dS and sums
- * the key blocks in ascending order in registers (dQ * scale and the
- * conversion are its epilogue: the pages' dQ postprocess, fused).  No atomics
+ * Two launches on `stream`: a Q-stationary kernel for dQ that first runs the
+ * preprocess for its own query rows (Delta from O and dO, written to the
+ * workspace with LSE * log2(e)), then recomputes dS and sums the key blocks
+ * in ascending order in registers (dQ * scale and the conversion are its
+ * epilogue: the pages' dQ postprocess, fused); then a KV-stationary kernel
+ * for dK and dV that reads the workspace rows.  No atomics
  * are used, so every output is bit-identical from run to run; `deterministic`
  * is accepted and always satisfied.
  * Sq == 0 gives dK = dV = 0; Sk == 0 gives dQ = 0.
@@ -161,13 +163,15 @@ attn_status attn_bwd(const attn_params *p, const void *q, const void *k, const v
 
 /*
  * The same backward pass, launching only the kernels selected in `phases`
- * (bitwise OR of ATTN_PHASE_*): the preprocess, then dK/dV, then dQ.
+ * (bitwise OR of ATTN_PHASE_*), in the order preprocess, dQ, dK/dV.
  * attn_bwd == attn_bwd_phases(..., ATTN_PHASE_ALL).  Lets a caller time or
- * schedule the kernels separately.  The dK/dV and dQ kernels read Delta and
- * LSE * log2(e) from `workspace`, which the preprocess writes, so the
- * preprocess must have run on the same workspace first; a gradient phase
- * whose statistics were not produced that way gives unspecified (but
- * in-bounds) results.  Arguments, validation and errors as
+ * schedule the kernels separately.  The dQ kernel computes Delta itself and
+ * writes Delta and LSE * log2(e) to `workspace`, so ATTN_PHASE_PREPROCESS
+ * launches the standalone preprocess only when ATTN_PHASE_DQ is not also
+ * selected (then it writes the same workspace rows).  The dK/dV kernel reads
+ * them: a dK/dV phase needs the dQ phase or the preprocess to have run on the
+ * same workspace first, in this call or an earlier one; otherwise its results
+ * are unspecified (but in-bounds).  Arguments, validation and errors as
  * attn_bwd; phases == 0 or an unknown bit is ATTN_ERR_INVALID_ARGUMENT.
  */
 #define ATTN_PHASE_PREPROCESS 1u

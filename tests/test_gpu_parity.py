@@ -388,3 +388,66 @@ def test_strided_layouts_packed_kv_gqa(lib):
     torch.cuda.synchronize()
     ref = oracle_run(inp, False)
     _compare({"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": delta}, ref, "fp16")
+
+
+# The phase API: the dQ kernel runs the preprocess for its own rows, so
+# DQ then DKDV is the full backward; the standalone preprocess (PREPROCESS
+# without DQ) writes the same workspace rows for a later dK/dV launch.
+PHASE_CASES = [
+    ("phases_bf16_causal_ragged_d128", "bf16", 2, 4, 2, 200, 200, 128, True, None),
+    ("phases_fp16_varlen_d96", "fp16", 4, 4, 2, 0, 0, 96, True, ([1, 130, 257, 64], [1, 130, 257, 64])),
+    ("phases_bf16_gqa_d256", "bf16", 1, 4, 2, 150, 170, 256, False, None),
+]
+
+
+@pytest.mark.parametrize("case", PHASE_CASES, ids=[c[0] for c in PHASE_CASES])
+def test_phases_split_matches_full(lib, case):
+    import torch
+    print(f"[gpu] phases {case[0]}", flush=True)
+    inp = _inputs(case, seed=77)
+    name, dt, causal = case[0], case[1], case[8]
+    q, k, v, do = (upload(inp[n + "_bits"], dt) for n in ("q", "k", "v", "do"))
+    kw = {}
+    if "cu_seqlens_q" in inp:
+        kw = dict(cu_seqlens_q=torch.from_numpy(inp["cu_seqlens_q"]).cuda(),
+                  cu_seqlens_k=torch.from_numpy(inp["cu_seqlens_k"]).cuda(),
+                  max_seqlen_q=int(inp["lengths_q"].max()), max_seqlen_k=int(inp["lengths_k"].max()))
+    scale = 1.0 / math.sqrt(q.shape[-1])
+    o, lse = lib.attn_fwd(q, k, v, causal=causal, softmax_scale=scale, **kw)
+    p = lib.make_params(q, k, causal, scale, False, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"),
+                        kw.get("max_seqlen_q"), kw.get("max_seqlen_k"))
+    nbytes = max(lib.bwd_workspace_size(p), 256)
+
+    def fresh_ws():  # NaN bit patterns: a phase that reads unwritten rows shows up
+        return torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+
+    def outs():
+        return torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    full = lib.attn_bwd(q, k, v, o, lse, do, causal=causal, softmax_scale=scale, return_delta=True,
+                        workspace=fresh_ws(), **kw)
+    # dQ (with its preprocess), then dK/dV in a second call on the same workspace
+    ws = fresh_ws()
+    dq, dk, dv = outs()
+    common = dict(causal=causal, softmax_scale=scale, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    r1 = lib.attn_bwd(q, k, v, o, lse, do, phases=lib.PHASE_DQ, return_delta=True, **common)
+    lib.attn_bwd(q, k, v, o, lse, do, phases=lib.PHASE_DKDV, **common)
+    torch.cuda.synchronize()
+    for a_, b_, n in ((dq, full[0], "dq"), (dk, full[1], "dk"), (dv, full[2], "dv"), (r1[3], full[3], "delta")):
+        assert torch.equal(a_.view(torch.int16) if a_.dtype != torch.float32 else a_.view(torch.int32),
+                           b_.view(torch.int16) if b_.dtype != torch.float32 else b_.view(torch.int32)), n
+    # the standalone preprocess, then dK/dV and dQ one call each
+    ws = fresh_ws()
+    dq, dk, dv = outs()
+    common = dict(causal=causal, softmax_scale=scale, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
+    r0 = lib.attn_bwd(q, k, v, o, lse, do, phases=lib.PHASE_PREPROCESS, return_delta=True, **common)
+    lib.attn_bwd(q, k, v, o, lse, do, phases=lib.PHASE_DKDV, **common)
+    lib.attn_bwd(q, k, v, o, lse, do, phases=lib.PHASE_DQ, **common)
+    torch.cuda.synchronize()
+    assert torch.equal(dq.view(torch.int16), full[0].view(torch.int16)), "dq"
+    ref = oracle_run(inp, causal)
+    got = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "delta": r0[3]}
+    _compare(got, ref, dt)
+    # both preprocess paths give Delta to fp32 rounding
+    d0, d1 = to_f64(r0[3]), to_f64(full[3])
+    assert np.abs(d0 - d1).max() <= 1e-5 * max(1.0, np.abs(d1).max())
