@@ -287,6 +287,10 @@ void attn_bwd_dkdv_kernel(Args a) {
             const int e = 8 * jj + r;
             p = (key_ok && e >= e_lo && e <= e_hi) ? p : 0.f;
           }
+          // keeps the exp between the dP products it is written between:
+          // the scheduling fences order only side effects, and the compiler
+          // otherwise sinks all 16 exps below the last product
+          asm volatile("" : "+v"(p));
           sacc[j] = p;
         };
         sched_fence();
