@@ -34,6 +34,8 @@ constexpr int kFwdBN = 64;   // key rows per iteration
 // by more than this, so P <= 2^8 = 256: exact in fp32 sums, and within the
 // fp16 and bf16 range of the P operand.
 constexpr float kFwdRescaleSlack = 8.f;
+// LDS operand reads in flight ahead of their product
+constexpr int kFwdPD = 4;
 
 // Head dims up to 128 run two waves per SIMD; the 256-wide tile (Q and the
 // O accumulator in registers) runs one.
@@ -159,16 +161,39 @@ void attn_fwd_kernel(Args a) {
     const int sbase = st * STAGE;
 
     // S^T (keys x queries) for this lane's 32 query columns.
+    // The K operands are read kFwdPD products ahead (a ring of registers),
+    // so each product waits for a read issued several products earlier.
     f32x16 sc[TK];
 #pragma unroll
-    for (int tk = 0; tk < TK; ++tk) {
-      sc[tk] = f32x16{};
+    for (int tk = 0; tk < TK; ++tk) sc[tk] = f32x16{};
+    {
+      constexpr int NSD = DC / 16, NS = TK * NSD, PD = kFwdPD;
+      u32x4 fr[PD];
+      auto rd = [&](int i, int slot) {  // step i: key tile i / NSD, head-dim step i % NSD
+        fr[slot] = lds_rd128(smem, (sbase + 32 * (i / NSD) * RB + kvb) ^ (32 * (i % NSD)));
+      };
+      sched_fence();
 #pragma unroll
-      for (int sd = 0; sd < DC / 16; ++sd) {
-        const u32x4 af = lds_rd128(smem, (sbase + 32 * tk * RB + kvb) ^ (32 * sd));
-        sc[tk] = mfma32<BF16>(af, qf[sd], sc[tk]);
+      for (int i = 0; i < PD; ++i) rd(i, i);
+      sched_fence();
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const u32x4 op = fr[i % PD];
+        if (i + PD < NS) rd(i + PD, i % PD);
+        sc[i / NSD] = mfma32<BF16>(op, qf[i % NSD], sc[i / NSD]);
+        sched_fence();
       }
     }
+    // The first V^T operands of O^T += V^T P^T do not depend on P: read them
+    // now, under the softmax.
+    constexpr int NO = TK * 2 * TD, PDO = kFwdPD;
+    u32x4 fb[PDO];
+    auto rdo = [&](int i, int slot) {  // step i: key tile, 16-key step, head-dim tile
+      const int ro = sbase + TILE + (32 * (i / (2 * TD)) + 16 * ((i / TD) % 2)) * RB;
+      fb[slot] = tr_frag_b(smem, ro + va[i % TD], ro + vb[i % TD]);
+    };
+#pragma unroll
+    for (int i = 0; i < PDO; ++i) rdo(i, i);
 
     // Mask (only on tiles crossing an edge of the band or the last key),
     // row max over keys, exp2 with scale*log2(e) folded into the fma.
@@ -268,20 +293,22 @@ void attn_fwd_kernel(Args a) {
     }
 
     // O^T += V^T P^T: P^T leaves the MFMA in B-operand layout (k = keys).
+    u32x4 pf[TK][2];
 #pragma unroll
     for (int tk = 0; tk < TK; ++tk) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
-        u32x4 pf;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pf[e] = pack2<BF16>(sc[tk][8 * s2 + 2 * e], sc[tk][8 * s2 + 2 * e + 1]);
-        const int ro = sbase + TILE + (32 * tk + 16 * s2) * RB;
-#pragma unroll
-        for (int t = 0; t < TD; ++t) {
-          const u32x4 vf = tr_frag_b(smem, ro + va[t], ro + vb[t]);
-          oacc[t] = mfma32<BF16>(vf, pf, oacc[t]);
-        }
+        for (int e = 0; e < 4; ++e) pf[tk][s2][e] = pack2<BF16>(sc[tk][8 * s2 + 2 * e], sc[tk][8 * s2 + 2 * e + 1]);
       }
+    }
+    sched_fence();
+#pragma unroll
+    for (int i = 0; i < NO; ++i) {
+      const u32x4 op = fb[i % PDO];
+      if (i + PDO < NO) rdo(i + PDO, i % PDO);
+      oacc[i % TD] = mfma32<BF16>(op, pf[i / (2 * TD)][(i / TD) % 2], oacc[i % TD]);
+      sched_fence();
     }
     wait_vmcnt<0>();  // block nb + 1 landed (this wave's share)
     lds_barrier();    // everyone's share; every wave is done with stage st
