@@ -563,43 +563,72 @@ void attn_bwd_dq_wide_kernel(Args a) {
     const int ta = tab + (n % NSTAGE) * STAGE, tb = tbb + (n % NSTAGE) * STAGE;
     const bool masked = (BANDED && (n * BN + BN - 1 > qw + off_causal + a.win_r || n * BN < qw + 31 + off_causal - a.win_l)) ||
                         (n * BN + BN > s.sk);
+    // One wave per SIMD: every product's LDS operand is read kDqPD steps
+    // ahead through a register ring, and each half's softmax runs one
+    // element per product under the next products (half 0 under half 1's
+    // S^T/dP^T, half 1 under half 0's dQ); the exps are pinned there (the
+    // scheduling fences order only side effects).
     f32x16 sc[2], pc[2];
+    u32x4 ds[2][2];
+    auto soft = [&](int kh, int j) {  // dS^T element j of half kh, packed in pairs
+      float t = __builtin_fmaf(sc[kh][j], a.scale_log2, -L2);
+      const int ks = n * BN + 32 * kh + 8 * (j >> 2) + (j & 3);
+      if (masked) t = (ks <= kv_hi && ks >= kv_lo) ? t : -__builtin_inff();
+      float pv = fast_exp2(t);
+      asm volatile("" : "+v"(pv));
+      pc[kh][j] = pv * (pc[kh][j] + Dl);  // Dl holds -Delta
+      if (j & 1) ds[kh][j >> 3][(j & 7) >> 1] = pack2<BF16>(pc[kh][j - 1], pc[kh][j]);
+    };
+    {
+      // step i: half i / NSD, head-dim step i % NSD; a K and a V fragment
+      constexpr int NS = 2 * NSD, PD = kDqPD;
+      u32x4 fk[PD], fv[PD];
+      auto rd = [&](int i, int slot) {
+        const int o = (sv ^ (32 * (i % NSD))) + 32 * (i / NSD) * RB;
+        fk[slot] = lds_rd128(smem, o);
+        fv[slot] = lds_rd128(smem, o + KT);
+      };
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      sc[kh] = f32x16{};
-      pc[kh] = f32x16{};
+      for (int kh = 0; kh < 2; ++kh) {
+        sc[kh] = f32x16{};
+        pc[kh] = f32x16{};
+      }
+      sched_fence();
 #pragma unroll
-      for (int sd = 0; sd < NSD; ++sd) {
-        const int o = (sv ^ (32 * sd)) + 32 * kh * RB;
-        const u32x4 ka = lds_rd128(smem, o);
-        const u32x4 va = lds_rd128(smem, o + KT);
+      for (int i = 0; i < PD; ++i) rd(i, i);
+      sched_fence();
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int kh = i / NSD, sd = i % NSD;
+        const u32x4 ka = fk[i % PD], va = fv[i % PD];
+        if (i + PD < NS) rd(i + PD, i % PD);
         sc[kh] = mfma32<BF16>(ka, qf[sd], sc[kh]);
         pc[kh] = mfma32<BF16>(va, df[sd], pc[kh]);
+        if (kh == 1) soft(0, sd);
+        sched_fence();
       }
     }
-    u32x4 ds[2][2];
+    {
+      // step i: half i / (2*TD), 16-key step (i / TD) % 2, head-dim tile i % TD
+      constexpr int NQ = 4 * TD, PD = kDqPD;
+      u32x4 fb[PD];
+      auto rd = [&](int i, int slot) {
+        const int ro = (32 * (i / (2 * TD)) + 16 * ((i / TD) % 2)) * RB;
+        const int t = i % TD;
+        fb[slot] = tr_frag_b(smem, (ta ^ (64 * t)) + ro, (tb ^ (64 * t)) + ro);
+      };
+      sched_fence();
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+      for (int i = 0; i < PD; ++i) rd(i, i);
+      sched_fence();
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float t = __builtin_fmaf(sc[kh][j], a.scale_log2, -L2);
-        const int ks = n * BN + 32 * kh + 8 * (j >> 2) + (j & 3);
-        if (masked) t = (ks <= kv_hi && ks >= kv_lo) ? t : -__builtin_inff();
-        const float pv = fast_exp2(t);
-        pc[kh][j] = pv * (pc[kh][j] + Dl);  // Dl holds -Delta
-        if (j & 1) ds[kh][j >> 3][(j & 7) >> 1] = pack2<BF16>(pc[kh][j - 1], pc[kh][j]);
-      }
-    }
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int ro = (32 * kh + 16 * s2) * RB;
-#pragma unroll
-        for (int t = 0; t < TD; ++t) {
-          const u32x4 kb = tr_frag_b(smem, (ta ^ (64 * t)) + ro, (tb ^ (64 * t)) + ro);
-          dq_acc[t] = mfma32<BF16>(ds[kh][s2], kb, dq_acc[t]);
-        }
+      for (int i = 0; i < NQ; ++i) {
+        const int kh = i / (2 * TD), s2 = (i / TD) % 2;
+        const u32x4 kb = fb[i % PD];
+        if (i + PD < NQ) rd(i + PD, i % PD);
+        dq_acc[i % TD] = mfma32<BF16>(ds[kh][s2], kb, dq_acc[i % TD]);
+        if (i < 16) soft(1, i);
+        sched_fence();
       }
     }
   }
