@@ -13,7 +13,10 @@
 // The transposed score tile puts one query per lane, so LSE and Delta are
 // per-lane constants, and dS^T leaves the MFMA in the A-operand layout of
 // dQ = dS K.  The softmax scale is applied once, in the epilogue, which is
-// the pages' dQ postprocess (scale, convert) fused.
+// the pages' dQ postprocess (scale, convert) fused.  Each kernel also runs
+// the preprocess for its own query rows first (Delta = rowsum(O o dO) from
+// O loaded beside dO, and LSE*log2(e)) and writes both to the workspace for
+// the dK/dV kernel, which is launched after it.
 #pragma once
 
 #include <type_traits>

@@ -8,7 +8,8 @@
 // the row sum.  The stored statistic is converted to natural log, the form the
 // flash-attention CK mha_bwd.cpp page's softmax_lse takes.
 //
-// gfx950 design (not the page's): 4 wave64s, each owning 32 query rows; the
+// gfx950 design (not the page's): wave64s each owning 32 query rows (8 per
+// workgroup, two per SIMD, up to head dim 128; 4 for the 256-wide tile); the
 // score tile is computed transposed, S^T = K Q^T, so that every lane holds one
 // query row (its column) -- the row max / row sum need only an in-lane
 // reduction plus one exchange between the two lane halves, and the
@@ -18,7 +19,8 @@
 // the whole kernel; K/V blocks come straight from global memory into two LDS
 // stages (direct global->LDS loads, one block ahead), laid out with the
 // 16-byte-chunk swizzle that keeps both the row reads of K and the transposed
-// reads of V free of bank conflicts.
+// reads of V free of bank conflicts, and each product's operand is read a
+// few products ahead through a ring of registers.
 #pragma once
 
 #include "attn_device.h"
