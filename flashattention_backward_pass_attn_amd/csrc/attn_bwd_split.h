@@ -35,10 +35,16 @@ namespace attn {
 
 constexpr int kDkvBM = 64;    // query rows per iteration of the dK/dV kernel
 // Key rows per dK/dV workgroup: 16 per wave.  Head dims up to 128 run 8 waves
-// (two per SIMD, 128 keys); the 256-wide tile runs 4 waves (one per SIMD,
-// 64 keys), whose K, V and accumulators take twice the registers.
+// (two per SIMD, 128 keys, one workgroup per CU); the 256-wide tile runs 4
+// waves (one per SIMD, 64 keys), whose K, V and accumulators take twice the
+// registers.  Causal MHA at head dims up to 128 can also run 4 waves (64
+// keys) with two workgroups per CU, so that one workgroup's start-up and
+// epilogue overlap the other's tile loop (the host picks it; see
+// dkdv_small_wg in the launcher).
 constexpr int dkdv_waves(int d) { return d > 128 ? 4 : 8; }
 constexpr int dkdv_bn(int d) { return 16 * dkdv_waves(d); }
+// waves per SIMD of a dK/dV kernel with NW waves per workgroup
+constexpr int dkdv_wpe(int d, int nw) { return nw == 8 || d <= 128 ? 2 : 1; }
 
 // ---------------------------------------------------------------------------
 // dK / dV: one workgroup per (key block, KV head, sequence) -- 128 keys, or
@@ -58,12 +64,15 @@ constexpr int dkdv_bn(int d) { return 16 * dkdv_waves(d); }
 // dS exchange (8 x 2 KiB); the block's K and V pass through the last stage
 // and the bytes after it on their way into registers.
 // ---------------------------------------------------------------------------
-template <bool BF16, int D, int DC, bool BANDED>
-__global__ __launch_bounds__(64 * dkdv_waves(D)) __attribute__((amdgpu_waves_per_eu(dkdv_waves(D) / 4, dkdv_waves(D) / 4)))
+template <bool BF16, int D, int DC, bool BANDED, int NW = dkdv_waves(D)>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(dkdv_wpe(D, NW), dkdv_wpe(D, NW))))
 void attn_bwd_dkdv_kernel(Args a) {
   static_assert(DC % 32 == 0 && DC <= D, "compute width: 32-column tiles within the stored tile");
-  constexpr int NW = dkdv_waves(D);
-  constexpr int BM = kDkvBM, BN = dkdv_bn(D);
+  static_assert(NW == 8 ? D <= 128 : NW == 4, "8 waves up to head dim 128, else 4");
+  constexpr int BM = kDkvBM, BN = 16 * NW;
+  // LDS operand reads in flight ahead of their product (two for the 4-wave
+  // kernel at two workgroups per CU, which has 256 registers per wave)
+  constexpr int PDK = NW == 4 && D <= 128 ? 2 : 3;
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int RB = D * 2;                  // bytes per row
   constexpr int TILE = BM * RB;
@@ -273,7 +282,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       // (matrix-core work only) and fills the gaps.
       f32x16 sacc = f32x16{};
       {
-        constexpr int NS = DC / 16, PD = 3;
+        constexpr int NS = DC / 16, PD = PDK;
         u32x4 fr[PD];
         // operand step i: Q for i < NS (S chain), dO for i >= NS (dP chain)
         auto rd = [&](int i, int slot) {
@@ -361,7 +370,7 @@ void attn_bwd_dkdv_kernel(Args a) {
       u32x4 par[2];
       par[0] = *reinterpret_cast<const u32x4*>(xpar + 0 * 1024);
       par[1] = *reinterpret_cast<const u32x4*>(xpar + 1 * 1024);
-      constexpr int NS = 4 * TD, PD = 3;
+      constexpr int NS = 4 * TD, PD = PDK;
       u32x4 fb[PD];
       auto rd = [&](int i, int slot) {
         const int sq = (i / TD + 2 * R) & 3, t = i % TD;
