@@ -35,6 +35,11 @@ SMALL_CASES = [
     ("d80_bf16_causal_gqa", "bf16", 2, 4, 2, 190, 190, 80, True, None),
     ("d72_fp16_noncausal_sq_lt_sk", "fp16", 1, 2, 2, 140, 203, 72, False, None),
     ("d104_fp16_causal", "fp16", 1, 2, 1, 160, 160, 104, True, None),
+    # causal MHA at fixed lengths runs the four-wave dK/dV kernel (64-key
+    # blocks): the 96-wide compute tile, a ragged last block, Sq != Sk
+    ("d96_bf16_causal_mha_ragged", "bf16", 2, 2, 2, 190, 190, 96, True, None),
+    ("d80_fp16_causal_mha_sq_gt_sk", "fp16", 1, 3, 3, 230, 101, 80, True, None),
+    ("ragged_bf16_causal_mha_d128", "bf16", 2, 4, 4, 200, 200, 128, True, None),
 ]
 
 
