@@ -366,11 +366,21 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   if (stat_row >= 0) store_row_stats(a.delta, a.lse2, a.delta_out, stat_row, h, L2, Dl);
 #pragma unroll
   for (int j = 0; j < 16; ++j) ndl[j] = Dl;
+  // Tiles [n_begin, v_end) hold a key some row of this wave sees; past its
+  // last row's diagonal (or band edge), and for a wave whose rows are all
+  // past the end, the wave still loads and takes every barrier but issues
+  // no products: those tiles would add exact zeros.
+  int v_end = n_begin;
+  if (qw < s.sq) {
+    const int last_key = BANDED ? min(qw + 31, s.sq - 1) + off_causal + a.win_r : s.sk - 1;
+    if (last_key >= 0) v_end = min(n_end, max(n_begin, last_key / BN + 1));
+  }
   if (n_begin < n_end) {
     wait_vmcnt<0>();
     lds_barrier();
     if (n_begin + 1 < n_end) prefetch(n_begin + 1);
-    if (tile_masked(n_begin)) {
+    if (v_end == n_begin) {
+    } else if (tile_masked(n_begin)) {
       run(n_begin, std::true_type{}, std::false_type{}, std::true_type{});
     } else {
       run(n_begin, std::true_type{}, std::false_type{}, std::false_type{});
@@ -384,8 +394,9 @@ void attn_bwd_dq_recompute_kernel(Args a) {
       const int hi = qw + off_causal + a.win_r - (BN - 1);
       u_hi = hi < 0 ? 0 : min(u_hi, hi / BN + 1);
     }
+    u_hi = min(u_hi, v_end);
     int n = n_begin + 1;
-    const int e1 = min(u_lo, n_end);
+    const int e1 = min(min(u_lo, n_end), v_end);
     for (; n < e1; ++n) {
       wait_vmcnt<0>();
       lds_barrier();
@@ -398,13 +409,29 @@ void attn_bwd_dq_recompute_kernel(Args a) {
       if (n + 1 < n_end) prefetch(n + 1);
       run(n, std::false_type{}, std::false_type{}, std::false_type{});
     }
-    for (; n < n_end; ++n) {
+    for (; n < v_end; ++n) {
       wait_vmcnt<0>();
       lds_barrier();
       if (n + 1 < n_end) prefetch(n + 1);
       run(n, std::false_type{}, std::false_type{}, std::true_type{});
     }
-    run(n_end, std::false_type{}, std::true_type{}, std::false_type{});
+    // here n == v_end unless the wave saw no tile
+    if (v_end > n_begin) {
+      if (v_end < n_end) {
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (n + 1 < n_end) prefetch(n + 1);
+        run(n, std::false_type{}, std::true_type{}, std::false_type{});
+        ++n;
+      } else {
+        run(n_end, std::false_type{}, std::true_type{}, std::false_type{});
+      }
+    }
+    for (; n < n_end; ++n) {
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (n + 1 < n_end) prefetch(n + 1);
+    }
   }
 
   // ---- dQ * scale, rounded to nearest even: the pages' postprocess, fused.
