@@ -40,6 +40,10 @@ SMALL_CASES = [
     ("d96_bf16_causal_mha_ragged", "bf16", 2, 2, 2, 190, 190, 96, True, None),
     ("d80_fp16_causal_mha_sq_gt_sk", "fp16", 1, 3, 3, 230, 101, 80, True, None),
     ("ragged_bf16_causal_mha_d128", "bf16", 2, 4, 4, 200, 200, 128, True, None),
+    # the 64-wide tile: varlen with an empty and a short sequence, a 48-wide
+    # head with Sq > Sk
+    ("varlen_bf16_causal_d64_ragged", "bf16", 4, 4, 2, 0, 0, 64, True, ([33, 0, 200, 129], [33, 0, 200, 129])),
+    ("d48_fp16_noncausal_sq_gt_sk", "fp16", 1, 2, 2, 260, 150, 48, False, None),
 ]
 
 
