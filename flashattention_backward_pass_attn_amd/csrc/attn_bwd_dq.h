@@ -72,7 +72,8 @@ struct DqSchedule {
 // ---------------------------------------------------------------------------
 // dQ for head dims up to 128: one workgroup per (query head x sequence,
 // 256-query block), 8 waves (two per SIMD), wave w owning queries 32w .. +32
-// of the block; each wave works every 64-key tile alone as two 32-key halves.
+// of the block; each wave works the 64-key tiles its rows see alone, as two
+// 32-key halves.
 // K and V tiles are stored D wide in LDS (D = 64 or 128) and the products run
 // DC wide (96 for head dims 72-96).
 //
@@ -355,8 +356,8 @@ void attn_bwd_dq_recompute_kernel(Args a) {
   // that need no mask run in one loop and the masked ones (the band's left
   // edge, its right edge or diagonal, the ragged last tile) in loops of
   // their own, so the matrix-core accumulators flow through straight loops
-  // rather than branches.  A wave runs every tile of the block (tiles it
-  // cannot see add exact zeros), so every wave takes the same barriers.
+  // rather than branches.  Every wave loads its share of every tile of the
+  // block and takes every barrier, also for the tiles it skips (below).
   if (n_begin < n_end) prefetch(n_begin);
   // The preprocess for this wave's rows, under the first tile's loads:
   // -Delta from O and dO, and the workspace rows that the dK/dV kernel
@@ -380,6 +381,7 @@ void attn_bwd_dq_recompute_kernel(Args a) {
     lds_barrier();
     if (n_begin + 1 < n_end) prefetch(n_begin + 1);
     if (v_end == n_begin) {
+      // this wave sees no key of the block: loads and barriers only
     } else if (tile_masked(n_begin)) {
       run(n_begin, std::true_type{}, std::false_type{}, std::true_type{});
     } else {
