@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 # per-kernel register, scratch and LDS use reported by the compiler for the
 # last build (tests/test_build_resources.py checks that no kernel spills)
 RESOURCES_PATH = os.path.join(PKG_DIR, "libattn_resources.txt")
+# gfx950 assembly of the same build (tests/test_build_resources.py checks the
+# wait states before every inline-asm direct global->LDS load)
+ASM_PATH = os.path.join(PKG_DIR, "libattn_device.s")
 SOURCES = [os.path.join(CSRC, "attn_api.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("attn_device.h", "attn_fwd.h", "attn_bwd.h", "attn_bwd_split.h",
                                               "attn_bwd_dq.h")] + [os.path.join(ROOT, "include", "attn.h")]
@@ -61,6 +64,12 @@ def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH) -> 
     if out_path == LIB_PATH:
         with open(RESOURCES_PATH, "w") as f:
             f.write("\n".join(remarks) + "\n")
+        asm = [hipcc_path(), *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")], *(extra_flags or []),
+               "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", ASM_PATH]
+        res = subprocess.run(asm, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError("hipcc failed writing the device assembly")
     return out_path
 
 

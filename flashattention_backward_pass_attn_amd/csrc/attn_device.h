@@ -349,12 +349,21 @@ __device__ __forceinline__ u32x4 make_srd(const void* base, int64_t num_bytes) {
   return r;
 }
 
+// The compiler does not see into the asm, so it inserts no wait states for
+// it.  An LDS DMA reading M0 one instruction after a scalar write of M0 (the
+// compiler sets M0 for the "{m0}" operand right before the asm) needs one:
+// the s_nop supplies it.  The descriptor's scalar registers must not have
+// been written by a vector instruction (readfirstlane, a spill reload)
+// within the five instructions before the load; the build's test of the
+// generated assembly checks that for every direct load.
 __device__ __forceinline__ void dma16(u32x4 srd, int off, uint32_t lds_byte) {
-  __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte) : "memory");
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte)
+                   : "memory");
 }
 
 __device__ __forceinline__ void dma4(u32x4 srd, int off, uint32_t lds_byte) {
-  __asm__ volatile("buffer_load_dword %0, %1, 0 offen lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte) : "memory");
+  __asm__ volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" :: "v"(off), "s"(srd), "{m0}"(lds_byte)
+                   : "memory");
 }
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding:
