@@ -51,10 +51,20 @@ def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH) -> 
            "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
+    # the device assembly of the same sources and flags, compiled alongside
+    asm_proc = None
+    if out_path == LIB_PATH:
+        asm = [hipcc_path(), *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")], *(extra_flags or []),
+               "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", ASM_PATH]
+        asm_proc = subprocess.Popen(asm, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
+    asm_out = asm_proc.communicate() if asm_proc is not None else ("", "")
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building libattn.so")
+    if asm_proc is not None and asm_proc.returncode != 0:
+        sys.stderr.write(asm_out[0] + asm_out[1])
+        raise RuntimeError("hipcc failed writing the device assembly")
     remarks = [ln.split("remark:", 1)[1].split("[-Rpass-analysis")[0].rstrip()
                for ln in res.stderr.splitlines() if "remark:" in ln and "kernel-resource-usage" in ln]
     other = [ln for ln in res.stderr.splitlines() if "kernel-resource-usage" not in ln]
@@ -64,12 +74,6 @@ def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH) -> 
     if out_path == LIB_PATH:
         with open(RESOURCES_PATH, "w") as f:
             f.write("\n".join(remarks) + "\n")
-        asm = [hipcc_path(), *[f for f in HIPCC_FLAGS if f not in ("-fPIC", "-shared")], *(extra_flags or []),
-               "--cuda-device-only", "-S", "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", ASM_PATH]
-        res = subprocess.run(asm, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError("hipcc failed writing the device assembly")
     return out_path
 
 
